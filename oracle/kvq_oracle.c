@@ -1,0 +1,424 @@
+/*
+ * kvq_oracle.c -- plain, slow CPU reference ("oracle") for layer-wise mixed-precision
+ * KV-cache quantization and for single-token decode attention over the packed cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load this library.  The GPU library neither links nor calls it, and the
+ * two share no source, header, table or helper.
+ *
+ * What it computes, and where that comes from:
+ *   - Keys are quantized per channel (asymmetric, min/max over a group of tokens) because
+ *     keys carry channel-wise outliers; values are quantized per token (asymmetric, min/max
+ *     over a group of channels).
+ *       [Mixed-precision KV-cache quantization per-layer sensitivity (llms-explorer.com),
+ *        Facts: per-channel vs per-token keys]
+ *       [KVTuner OpenReview discussion (paperhub.cn/paper/zDwipF6h06), reply to reviewer 1,
+ *        section 4 "Per-channel vs. per-token quantization"; reply to reviewer 2, section 2
+ *        "Discussion of conflicting literature" (per-channel keys, per-token values)]
+ *   - Each layer carries its own (key bits, value bits) pair from an offline table; online,
+ *     only the newly generated token is quantized, at that layer's pair.
+ *       [KVTuner (mlsanity.com/paper/2502.04420), Abstract]
+ *       [KVTuner OpenReview discussion, reply to reviewer 3, section 1 "Computational cost"]
+ *   - Decode attention runs over the dequantized cache (FlashAttention-compatible method).
+ *       [KVTuner OpenReview discussion, reply to reviewer 2, section 1 "Efficiency evaluation
+ *        clarifications"]
+ *   - Format of this library: groups of 32 (32 tokens per key group, 32 channels per value
+ *     group), scale and zero stored as IEEE binary16, head_dim 128, bit widths {2,4,8}, and
+ *     the tokens that do not yet fill a 32-token group kept unquantized as bfloat16.
+ *
+ * Arithmetic: the codec runs in IEEE binary32 exactly as written below (every operation
+ * rounds to nearest-even; no contraction, no fast-math; SSE2 on x86-64), the attention runs
+ * in IEEE binary64.  The fp16 and bf16 conversions are written from the formats'
+ * definitions using exact binary64 arithmetic.
+ */
+#include <float.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "the oracle needs binary32 evaluation of float expressions (x86-64 SSE2)"
+#endif
+
+#define ORC_D 128     /* head dimension */
+#define ORC_G 32      /* tokens per key group == channels per value group == tokens per page */
+
+/* ------------------------------------------------------------------------------------ */
+/* binary16 / bfloat16 conversions                                                      */
+/* ------------------------------------------------------------------------------------ */
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Normal: (1024 + m) * 2^(e - 25); subnormal (e == 0): m * 2^-24. */
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* Round a binary32 value to the nearest binary16 value, ties to even. */
+uint16_t orc_f32_to_f16(float xf)
+{
+    double x = xf;
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | 0x7e00u);
+    double a = fabs(x);
+    if (isinf(a)) return (uint16_t)(sign | 0x7c00u);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);               /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    if (E < -14) E = -14;        /* subnormals share the spacing of the lowest normal binade */
+    double quantum = ldexp(1.0, E - 10);
+    double n = nearbyint(a / quantum);   /* exact quotient, rounded to integer, ties to even */
+    if (n == 0.0) return sign;
+    if (n >= 2048.0) { n /= 2.0; E += 1; }
+    if (E > 15) return (uint16_t)(sign | 0x7c00u);
+    if (n < 1024.0) return (uint16_t)(sign | (uint16_t)n);            /* subnormal */
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ * Normal: (128 + m) * 2^(e - 134); subnormal: m * 2^-133. */
+float orc_bf16_to_f32(uint16_t b)
+{
+    int sign = b >> 15, e = (b >> 7) & 255, m = b & 127;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133);
+    else if (e == 255)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + m), e - 134);
+    return (float)(sign ? -v : v);
+}
+
+/* Round a binary32 value to the nearest bfloat16 value, ties to even. */
+uint16_t orc_f32_to_bf16(float xf)
+{
+    double x = xf;
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | 0x7fc0u);
+    double a = fabs(x);
+    if (isinf(a)) return (uint16_t)(sign | 0x7f80u);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;
+    if (E < -126) E = -126;
+    double quantum = ldexp(1.0, E - 7);
+    double n = nearbyint(a / quantum);
+    if (n == 0.0) return sign;
+    if (n >= 256.0) { n /= 2.0; E += 1; }
+    if (E > 127) return (uint16_t)(sign | 0x7f80u);
+    if (n < 128.0) return (uint16_t)(sign | (uint16_t)n);
+    return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)(n - 128.0));
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* the group codec                                                                      */
+/* ------------------------------------------------------------------------------------ */
+
+static int valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
+
+/* Quantize one group of 32 values x[0], x[stride], ... to `bits`-bit unsigned codes.
+ *   mn, mx   : minimum and maximum of the group (binary32, exact)
+ *   s32      : (mx - mn) / (2^bits - 1), one binary32 subtraction and one binary32 division
+ *   s16, z16 : binary16 round-to-nearest-even of s32 and of mn  (the stored scale and zero)
+ *   code_i   : clamp(round_half_even((x_i - z) / s), 0, 2^bits - 1), with s, z the stored
+ *              binary16 values widened to binary32; every code is 0 when s == 0.
+ * Dequantization is code * s + z.  -0 inputs are read as +0 so the stored zero never
+ * depends on the order of a min over signed zeros. */
+int orc_quant_group(const float *x, int stride, int bits,
+                    uint16_t *s16_out, uint16_t *z16_out, uint8_t *codes)
+{
+    if (!valid_bits(bits)) return 1;
+    float v[ORC_G];
+    for (int i = 0; i < ORC_G; ++i) v[i] = x[(ptrdiff_t)i * stride] + 0.0f;
+    float mn = v[0], mx = v[0];
+    for (int i = 1; i < ORC_G; ++i) {
+        if (v[i] < mn) mn = v[i];
+        if (v[i] > mx) mx = v[i];
+    }
+    const float levels = (float)((1 << bits) - 1);
+    float range = mx - mn;
+    float s32 = range / levels;
+    uint16_t s16 = orc_f32_to_f16(s32);
+    uint16_t z16 = orc_f32_to_f16(mn);
+    float s = orc_f16_to_f32(s16);
+    float z = orc_f16_to_f32(z16);
+    for (int i = 0; i < ORC_G; ++i) {
+        if (s == 0.0f) { codes[i] = 0; continue; }
+        float d = v[i] - z;
+        float q = d / s;
+        float r = rintf(q);
+        if (r < 0.0f) r = 0.0f;
+        if (r > levels) r = levels;
+        codes[i] = (uint8_t)r;
+    }
+    *s16_out = s16;
+    *z16_out = z16;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* packed page layout (one page = 32 tokens of one KV head of one layer)                */
+/*                                                                                      */
+/*   offset 0            K codes, token-major: 32 rows of 16*kb bytes; token t, channel  */
+/*                       c sits at bit c*kb of row t (LSB-first, little-endian bytes)    */
+/*   offset 512*kb       K scale/zero: 128 words of 32 bits; word c = s16 | z16 << 16,   */
+/*                       the group of channel c over the page's 32 tokens                */
+/*   offset 512*kb+512   V codes, channel-major: 128 rows of 4*vb bytes; channel c,      */
+/*                       token t sits at bit t*vb of row c (LSB-first)                   */
+/*   offset 512*(kb+vb)+512  V scale/zero: 32 tokens x 4 groups of 32-bit words;         */
+/*                       word 4*t + j = s16 | z16 << 16 for channels 32j .. 32j+31       */
+/*   total 512*(kb+vb+2) bytes                                                           */
+/*                                                                                      */
+/* A layer's pool is [physical page][KV head][page bytes]; block_table[b][i] names the   */
+/* physical page that holds tokens 32i .. 32i+31 of sequence b.                         */
+/* ------------------------------------------------------------------------------------ */
+
+size_t orc_head_page_bytes(int kb, int vb) { return (size_t)512 * (size_t)(kb + vb + 2); }
+
+static size_t off_kcodes(int kb, int vb) { (void)kb; (void)vb; return 0; }
+static size_t off_ksz(int kb, int vb) { (void)vb; return (size_t)512 * kb; }
+static size_t off_vcodes(int kb, int vb) { (void)vb; return (size_t)512 * kb + 512; }
+static size_t off_vsz(int kb, int vb) { return (size_t)512 * (kb + vb) + 512; }
+
+static void put_code(uint8_t *row, int idx, int bits, unsigned code)
+{
+    size_t bit = (size_t)idx * bits;
+    row[bit / 8] |= (uint8_t)(code << (bit % 8));
+}
+
+static unsigned get_code(const uint8_t *row, int idx, int bits)
+{
+    size_t bit = (size_t)idx * bits;
+    return (row[bit / 8] >> (bit % 8)) & ((1u << bits) - 1u);
+}
+
+static void put_u32(uint8_t *p, uint32_t w)
+{
+    p[0] = (uint8_t)w; p[1] = (uint8_t)(w >> 8); p[2] = (uint8_t)(w >> 16); p[3] = (uint8_t)(w >> 24);
+}
+
+static uint32_t get_u32(const uint8_t *p)
+{
+    return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+}
+
+/* Quantize one page: k and v point at token 0, channel 0 of a 32 x 128 fp32 tile whose
+ * consecutive tokens are `tok_stride` floats apart. */
+int orc_pack_page(const float *k, const float *v, int tok_stride, int kb, int vb, uint8_t *dst)
+{
+    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    memset(dst, 0, orc_head_page_bytes(kb, vb));
+    uint8_t codes[ORC_G];
+    uint16_t s16, z16;
+    /* keys: one group per channel, over the page's 32 tokens */
+    for (int c = 0; c < ORC_D; ++c) {
+        orc_quant_group(k + c, tok_stride, kb, &s16, &z16, codes);
+        for (int t = 0; t < ORC_G; ++t)
+            put_code(dst + off_kcodes(kb, vb) + (size_t)t * 16 * kb, c, kb, codes[t]);
+        put_u32(dst + off_ksz(kb, vb) + 4 * (size_t)c, (uint32_t)s16 | (uint32_t)z16 << 16);
+    }
+    /* values: one group per (token, 32 consecutive channels) */
+    for (int t = 0; t < ORC_G; ++t) {
+        for (int j = 0; j < ORC_D / ORC_G; ++j) {
+            orc_quant_group(v + (size_t)t * tok_stride + 32 * j, 1, vb, &s16, &z16, codes);
+            for (int i = 0; i < ORC_G; ++i)
+                put_code(dst + off_vcodes(kb, vb) + (size_t)(32 * j + i) * 4 * vb, t, vb, codes[i]);
+            put_u32(dst + off_vsz(kb, vb) + 4 * (size_t)(4 * t + j),
+                    (uint32_t)s16 | (uint32_t)z16 << 16);
+        }
+    }
+    return 0;
+}
+
+/* Decode one page into binary64 K and V tiles [32][128].  code * s + z is exact in
+ * binary64 (an 8-bit integer times a binary16 value plus a binary16 value). */
+int orc_dequant_page(const uint8_t *src, int kb, int vb, double *k, double *v)
+{
+    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    for (int c = 0; c < ORC_D; ++c) {
+        uint32_t w = get_u32(src + off_ksz(kb, vb) + 4 * (size_t)c);
+        double s = orc_f16_to_f32((uint16_t)(w & 0xffffu));
+        double z = orc_f16_to_f32((uint16_t)(w >> 16));
+        for (int t = 0; t < ORC_G; ++t) {
+            unsigned code = get_code(src + off_kcodes(kb, vb) + (size_t)t * 16 * kb, c, kb);
+            k[t * ORC_D + c] = (double)code * s + z;
+        }
+    }
+    for (int t = 0; t < ORC_G; ++t) {
+        for (int c = 0; c < ORC_D; ++c) {
+            uint32_t w = get_u32(src + off_vsz(kb, vb) + 4 * (size_t)(4 * t + c / 32));
+            double s = orc_f16_to_f32((uint16_t)(w & 0xffffu));
+            double z = orc_f16_to_f32((uint16_t)(w >> 16));
+            unsigned code = get_code(src + off_vcodes(kb, vb) + (size_t)c * 4 * vb, t, vb);
+            v[t * ORC_D + c] = (double)code * s + z;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* layer-level operations                                                               */
+/* ------------------------------------------------------------------------------------ */
+
+static float src_elem(const void *src, int is_bf16, size_t i)
+{
+    return is_bf16 ? orc_bf16_to_f32(((const uint16_t *)src)[i]) : ((const float *)src)[i];
+}
+
+static uint16_t src_to_bf16(const void *src, int is_bf16, size_t i)
+{
+    return is_bf16 ? ((const uint16_t *)src)[i] : orc_f32_to_bf16(((const float *)src)[i]);
+}
+
+/* Prefill: quantize-on-write of sequences of length seq_len[b] taken from
+ * k_src / v_src [batch][max_tokens][H][128] (bf16 or fp32).  Full 32-token groups go to
+ * the pages named by the block table; the last seq_len mod 32 tokens go, as bf16, to
+ * residual slot t mod 32 of resid_k / resid_v [batch][H][32][128]. */
+int orc_pack(int kb, int vb, int H, int batch, int max_tokens, int src_is_bf16,
+             const void *k_src, const void *v_src, const int32_t *seq_len,
+             const int32_t *block_table, int max_pages,
+             uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+{
+    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    const size_t hp = orc_head_page_bytes(kb, vb);
+    static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
+    for (int b = 0; b < batch; ++b) {
+        int L = seq_len[b];
+        if (L < 0 || L > max_tokens || L > 32 * max_pages) return 2;
+        int full = L / ORC_G;
+        for (int h = 0; h < H; ++h) {
+            for (int g = 0; g < full; ++g) {
+                for (int t = 0; t < ORC_G; ++t)
+                    for (int c = 0; c < ORC_D; ++c) {
+                        size_t i = (((size_t)b * max_tokens + (size_t)(g * ORC_G + t)) * H + h) * ORC_D + c;
+                        tk[t * ORC_D + c] = src_elem(k_src, src_is_bf16, i);
+                        tv[t * ORC_D + c] = src_elem(v_src, src_is_bf16, i);
+                    }
+                int32_t phys = block_table[(size_t)b * max_pages + g];
+                orc_pack_page(tk, tv, ORC_D, kb, vb, pages + ((size_t)phys * H + h) * hp);
+            }
+            for (int t = full * ORC_G; t < L; ++t)
+                for (int c = 0; c < ORC_D; ++c) {
+                    size_t i = (((size_t)b * max_tokens + (size_t)t) * H + h) * ORC_D + c;
+                    size_t r = (((size_t)b * H + h) * ORC_G + (size_t)(t % ORC_G)) * ORC_D + c;
+                    resid_k[r] = src_to_bf16(k_src, src_is_bf16, i);
+                    resid_v[r] = src_to_bf16(v_src, src_is_bf16, i);
+                }
+        }
+    }
+    return 0;
+}
+
+/* Decode-time write of one new token per sequence, at position pos[b] (the length before
+ * the write).  The token goes to residual slot pos mod 32; when that slot is 31 the 32
+ * residual tokens form a full group and are quantized into page pos / 32.
+ * k_new / v_new are bf16 [batch][H][128]. */
+int orc_append(int kb, int vb, int H, int batch, const uint16_t *k_new, const uint16_t *v_new,
+               const int32_t *pos, const int32_t *block_table, int max_pages,
+               uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+{
+    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    const size_t hp = orc_head_page_bytes(kb, vb);
+    static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
+    for (int b = 0; b < batch; ++b) {
+        int p = pos[b];
+        if (p < 0 || p >= 32 * max_pages) return 2;
+        int slot = p % ORC_G;
+        for (int h = 0; h < H; ++h) {
+            uint16_t *rk = resid_k + ((size_t)b * H + h) * ORC_G * ORC_D;
+            uint16_t *rv = resid_v + ((size_t)b * H + h) * ORC_G * ORC_D;
+            for (int c = 0; c < ORC_D; ++c) {
+                rk[slot * ORC_D + c] = k_new[((size_t)b * H + h) * ORC_D + c];
+                rv[slot * ORC_D + c] = v_new[((size_t)b * H + h) * ORC_D + c];
+            }
+            if (slot == ORC_G - 1) {
+                for (int i = 0; i < ORC_G * ORC_D; ++i) {
+                    tk[i] = orc_bf16_to_f32(rk[i]);
+                    tv[i] = orc_bf16_to_f32(rv[i]);
+                }
+                int32_t phys = block_table[(size_t)b * max_pages + p / ORC_G];
+                orc_pack_page(tk, tv, ORC_D, kb, vb, pages + ((size_t)phys * H + h) * hp);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Single-token decode attention of every query head over the seq_len[b] cached tokens:
+ * full pages 0 .. seq_len/32 - 1 (dequantized) and the seq_len mod 32 residual tokens
+ * (exact bf16).  Query head hq reads KV head hq / (Hq / H).  In binary64:
+ *   s_j = (sum_c q_c k_jc) / sqrt(128),  m = max_j s_j,  l = sum_j exp(s_j - m),
+ *   lse = m + ln l,  out_c = sum_j exp(s_j - m) v_jc / l.
+ * q is [batch][Hq][128] (bf16 or fp32); out is [batch][Hq][128]; lse is [batch][Hq]
+ * (may be NULL). */
+int orc_decode_attn(int kb, int vb, int Hq, int H, int batch, int q_is_bf16, const void *q,
+                    const int32_t *seq_len, const int32_t *block_table, int max_pages,
+                    const uint8_t *pages, const uint16_t *resid_k, const uint16_t *resid_v,
+                    double *out, double *lse)
+{
+    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    if (H <= 0 || Hq % H != 0) return 3;
+    const int G = Hq / H;
+    const size_t hp = orc_head_page_bytes(kb, vb);
+    for (int b = 0; b < batch; ++b) {
+        int L = seq_len[b];
+        if (L <= 0 || L > 32 * max_pages) return 2;
+        int full = L / ORC_G;
+        double *K = (double *)malloc(sizeof(double) * (size_t)L * ORC_D);
+        double *V = (double *)malloc(sizeof(double) * (size_t)L * ORC_D);
+        double *s = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!K || !V || !s) { free(K); free(V); free(s); return 4; }
+        for (int h = 0; h < H; ++h) {
+            /* this head's keys and values for all L tokens, as exact binary64 */
+            for (int g = 0; g < full; ++g) {
+                int32_t phys = block_table[(size_t)b * max_pages + g];
+                orc_dequant_page(pages + ((size_t)phys * H + h) * hp, kb, vb,
+                                 K + (size_t)g * ORC_G * ORC_D, V + (size_t)g * ORC_G * ORC_D);
+            }
+            const uint16_t *rk = resid_k + ((size_t)b * H + h) * ORC_G * ORC_D;
+            const uint16_t *rv = resid_v + ((size_t)b * H + h) * ORC_G * ORC_D;
+            for (int t = full * ORC_G; t < L; ++t)
+                for (int c = 0; c < ORC_D; ++c) {
+                    K[(size_t)t * ORC_D + c] = orc_bf16_to_f32(rk[(t % ORC_G) * ORC_D + c]);
+                    V[(size_t)t * ORC_D + c] = orc_bf16_to_f32(rv[(t % ORC_G) * ORC_D + c]);
+                }
+            for (int gq = 0; gq < G; ++gq) {
+                int hq = h * G + gq;
+                double qd[ORC_D];
+                for (int c = 0; c < ORC_D; ++c)
+                    qd[c] = src_elem(q, q_is_bf16, ((size_t)b * Hq + hq) * ORC_D + c);
+                double m = -INFINITY;
+                for (int t = 0; t < L; ++t) {
+                    double dot = 0.0;
+                    for (int c = 0; c < ORC_D; ++c) dot += qd[c] * K[(size_t)t * ORC_D + c];
+                    s[t] = dot / sqrt((double)ORC_D);
+                    if (s[t] > m) m = s[t];
+                }
+                double l = 0.0, acc[ORC_D];
+                for (int c = 0; c < ORC_D; ++c) acc[c] = 0.0;
+                for (int t = 0; t < L; ++t) {
+                    double p = exp(s[t] - m);
+                    l += p;
+                    for (int c = 0; c < ORC_D; ++c) acc[c] += p * V[(size_t)t * ORC_D + c];
+                }
+                for (int c = 0; c < ORC_D; ++c) out[((size_t)b * Hq + hq) * ORC_D + c] = acc[c] / l;
+                if (lse) lse[(size_t)b * Hq + hq] = m + log(l);
+            }
+        }
+        free(K); free(V); free(s);
+    }
+    return 0;
+}

@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-precision KV decode hot path on one MI355X.
+
+Default workload (the headline): a Llama-3.1-8B-shaped stack -- 32 layers, 32 query heads,
+8 KV heads, head_dim 128 -- with the 3.25-bit per-layer table (layers 0-2 and 31 K4V8, 24
+layers K4V2, 4 layers K2V2), batch 16, 4096 cached tokens per sequence.  One step is one
+decode step of the whole stack: for every layer, kvq_append of the new token (position
+4096) and kvq_decode_attn over the 4097 tokens.  Throughput follows the pages' definition:
+generated tokens per second = batch / step time
+[KVTuner OpenReview discussion (paperhub.cn/paper/zDwipF6h06), reply to reviewer 2,
+section 1, "Throughput definition"].
+
+Inputs are seeded synthetic tensors (synth/), generated on the device; the timed region
+starts with the packed cache resident in HBM.  The step is captured once as a HIP graph and
+replayed (no allocation or host work inside the timed region).
+
+Prints ONE JSON line.  Other workloads: --config qwen | pack | single.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+LLAMA_C325 = [(4, 8)] * 3 + [(4, 2)] * 24 + [(2, 2)] * 4 + [(4, 8)]
+QWEN_C40 = [(8, 4)] * 4 + [(4, 4)] * 4 + [(4, 2)] * 16 + [(8, 4)] * 4
+
+CONFIGS = {
+    "llama": dict(workload="llama3.1-8b-shape C3.25 decode step (append + attention, 32 layers)",
+                  pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=16, context=4096, n_outliers=3,
+                  seed=20250204),
+    "qwen": dict(workload="qwen2.5-7b-shape C4.0 decode step (append + attention, 28 layers)",
+                 pairs=QWEN_C40, n_q_heads=28, n_kv_heads=4, batch=64, context=8192, n_outliers=3,
+                 seed=20250205),
+    "single": dict(workload="single layer K8V4, GQA 4, 512 tokens, fp32 K/V/q (attention only)",
+                   pairs=[(8, 4)], n_q_heads=4, n_kv_heads=1, batch=1, context=512, n_outliers=4,
+                   seed=2024),
+    "pack": dict(workload="prefill pack, llama3.1-8b shape C3.25, 32768 tokens, batch 1 (32 layers)",
+                 pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=1, context=32768, n_outliers=3,
+                 seed=20250206),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_alg_bytes(kb, vb, batch, H, Hq, L):
+    """Bytes one decode-attention launch must move: the pages covering the attended tokens
+    (codes + fp16 scale/zero), the live bf16 residual tokens (K and V), q (bf16), out (fp32)
+    and lse (fp32)."""
+    full, nres = L // 32, L % 32
+    pages = batch * H * full * 512 * (kb + vb + 2)
+    resid = batch * H * nres * 128 * 2 * 2
+    return pages + resid + batch * Hq * 128 * 2 + batch * Hq * 128 * 4 + batch * Hq * 4
+
+
+def append_alg_bytes(batch, H):
+    """Read of the new K/V token and its write into the residual slot (no flush)."""
+    return 2 * (batch * H * 128 * 2) * 2
+
+
+class DecodeStack:
+    """Packed per-layer caches of a decode workload, resident on the device."""
+
+    def __init__(self, cfg, device):
+        import torch
+        import synth
+        import layer_wise_mixed_kvq_amd as kvq
+        self.cfg = cfg
+        self.kvq = kvq
+        pairs = cfg["pairs"]
+        self.model = kvq.Model(pairs, cfg["n_q_heads"], cfg["n_kv_heads"])
+        B, H, C = cfg["batch"], cfg["n_kv_heads"], cfg["context"]
+        self.B, self.H, self.Hq, self.C = B, H, cfg["n_q_heads"], C
+        self.L = C + 1
+        self.max_pages = (self.L + 31) // 32
+        self.block_table = torch.arange(B * self.max_pages, dtype=torch.int32, device=device).view(B, self.max_pages)
+        self.caches, self.q, self.k_new, self.v_new, self.out, self.lse = [], [], [], [], [], []
+        seed = cfg["seed"]
+        seq_len = torch.full((B,), C, dtype=torch.int32, device=device)
+        src_dtype = "f32" if cfg is CONFIGS["single"] else "bf16"
+        for l, _ in enumerate(pairs):
+            cache = kvq.LayerCache(self.model, l, B, self.max_pages, block_table=self.block_table, device=device)
+            cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
+            k = synth.fill(seed, synth.KIND_K, l, B, C, H, chan_mult=cm, dtype=src_dtype, device=device)
+            v = synth.fill(seed, synth.KIND_V, l, B, C, H, dtype=src_dtype, device=device)
+            kvq.kvq_pack(self.model, l, cache, k, v, seq_len)
+            del k, v
+            self.caches.append(cache)
+            self.k_new.append(synth.fill(seed, synth.KIND_K_NEW, l, B, 1, H, chan_mult=cm, device=device).view(B, H, 128))
+            self.v_new.append(synth.fill(seed, synth.KIND_V_NEW, l, B, 1, H, device=device).view(B, H, 128))
+            qd = "f32" if src_dtype == "f32" else "bf16"
+            self.q.append(synth.fill(seed, synth.KIND_Q, l, B, 1, self.Hq, dtype=qd, device=device).view(B, self.Hq, 128))
+            self.out.append(torch.empty((B, self.Hq, 128), dtype=torch.float32, device=device))
+            self.lse.append(torch.empty((B, self.Hq), dtype=torch.float32, device=device))
+        torch.cuda.synchronize()
+        self.pos = torch.full((B,), C, dtype=torch.int32, device=device)
+        self.seq_len = torch.full((B,), self.L, dtype=torch.int32, device=device)
+        self.workspace = kvq.new_workspace(self.model, B, self.L, 0, device)
+
+    def decode_layer(self, l):
+        self.kvq.kvq_decode_attn(self.model, l, self.caches[l], self.q[l], self.seq_len, self.L,
+                                 out=self.out[l], lse=self.lse[l], workspace=self.workspace)
+
+    def step(self, with_append=True):
+        for l in range(len(self.caches)):
+            if with_append:
+                self.kvq.kvq_append(self.model, l, self.caches[l], self.k_new[l], self.v_new[l], self.pos)
+            self.decode_layer(l)
+
+    def alg_bytes(self, with_append=True):
+        tot = 0
+        for (kb, vb) in self.cfg["pairs"]:
+            tot += decode_alg_bytes(kb, vb, self.B, self.H, self.Hq, self.L)
+            if with_append:
+                tot += append_alg_bytes(self.B, self.H)
+        return tot
+
+    def decode_bytes(self):
+        return [decode_alg_bytes(kb, vb, self.B, self.H, self.Hq, self.L) for kb, vb in self.cfg["pairs"]]
+
+
+def capture(fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def per_launch_durations(launch, n_items, reps):
+    """Event pairs around every launch, on the stream the kernels run on; a GPU-side sleep
+    first lets the host queue every launch ahead of the GPU so only kernel time is seen."""
+    import torch
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_items)]
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(40_000_000)
+    for r in range(reps):
+        for i in range(n_items):
+            evs[r][i][0].record()
+            launch(i)
+            evs[r][i][1].record()
+    torch.cuda.synchronize()
+    return [sum(evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)) / reps for i in range(n_items)]
+
+
+def cpu_baseline_decode(cfg, stack, n_seq):
+    """The CPU oracle, as it stands (single thread), on `n_seq` of the batch's sequences for
+    every layer: the same append + attention work of one decode step.  Packing the sample
+    (prefill) is not timed."""
+    import numpy as np
+    import oracle as orc
+    import synth
+    seed, H, Hq, C = cfg["seed"], cfg["n_kv_heads"], cfg["n_q_heads"], cfg["context"]
+    maxp = (C + 1 + 31) // 32
+    bt = np.arange(maxp, dtype=np.int32).reshape(1, maxp)
+    t_total = 0.0
+    for l, (kb, vb) in enumerate(cfg["pairs"]):
+        cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
+        for b in range(n_seq):
+            k = synth.fill(seed, synth.KIND_K, l, 1, C, H, b0=b, chan_mult=cm)
+            v = synth.fill(seed, synth.KIND_V, l, 1, C, H, b0=b)
+            kn = synth.fill(seed, synth.KIND_K_NEW, l, 1, 1, H, b0=b, chan_mult=cm).view(1, H, 128)
+            vn = synth.fill(seed, synth.KIND_V_NEW, l, 1, 1, H, b0=b).view(1, H, 128)
+            q = synth.fill(seed, synth.KIND_Q, l, 1, 1, Hq, b0=b).view(1, Hq, 128)
+            import torch
+            bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+            pages, rk, rv = orc.new_cache(kb, vb, H, 1, maxp)
+            orc.pack(kb, vb, bits(k), bits(v), [C], bt, pages, rk, rv)
+            t0 = time.perf_counter()
+            orc.append(kb, vb, bits(kn), bits(vn), [C], bt, pages, rk, rv)
+            orc.decode_attn(kb, vb, H, bits(q), [C + 1], bt, pages, rk, rv)
+            t_total += time.perf_counter() - t0
+    return t_total
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama", choices=sorted(CONFIGS))
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--roofline-reps", type=int, default=5)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} (WORLD_SIZE {world}) is not supported; "
+              "this decode path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import layer_wise_mixed_kvq_amd as kvq
+    kvq.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.config]
+    if args.config == "pack":
+        return bench_pack(cfg, args)
+
+    log(f"[bench] building {args.config} cache ...")
+    t0 = time.perf_counter()
+    stack = DecodeStack(cfg, dev)
+    log(f"[bench] cache built in {time.perf_counter() - t0:.1f} s")
+
+    with_append = args.config != "single"
+    step_fn = (lambda: stack.step(with_append))
+    if args.no_graph:
+        for _ in range(args.warmup):
+            step_fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            step_fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms, wall = e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
+    else:
+        g = capture(step_fn)
+        log("[bench] graph captured; timing")
+        ms, wall = time_graph(g, args.steps, args.warmup)
+    # attention-only step
+    g_attn = capture(lambda: stack.step(False))
+    ms_attn, _ = time_graph(g_attn, args.steps, 2)
+    log(f"[bench] step {ms:.4f} ms (attention only {ms_attn:.4f} ms)")
+
+    # live per-launch durations of the dominant kernel (decode attention), every layer
+    n_layers = len(cfg["pairs"])
+    durs = per_launch_durations(stack.decode_layer, n_layers, args.roofline_reps)
+    dbytes = stack.decode_bytes()
+    achieved = sum(dbytes) / (sum(durs) * 1e-3) / 1e9
+    log(f"[bench] decode kernel avg {sum(durs) / n_layers * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
+
+    step_bytes = stack.alg_bytes(with_append)
+    tokens_per_s = stack.B * 1000.0 / ms
+    cpu = None
+    if args.cpu_seqs > 0 and args.config != "single":
+        log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequences x {n_layers} layers ...")
+        t_cpu = cpu_baseline_decode(cfg, stack, args.cpu_seqs)
+        cpu = {"value": args.cpu_seqs / t_cpu, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{args.cpu_seqs} of {stack.B} sequences, all {n_layers} layers: append + binary64 "
+                         f"attention over {stack.L} tokens (packing of the sample not timed), single thread"}
+        log(f"[bench] CPU oracle {t_cpu:.1f} s -> {cpu['value']:.3f} tokens/s")
+
+    rec = {
+        "metric": "mixed-precision KV decode-attn tokens/s + packed-KV GB/s (% HBM peak), 1 GPU",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/fp32-acc, int2/4/8 codes",
+        "data": "synthetic (seeded Irwin-Hall N(0,1) K/V/q, 3 outlier key channels x10 per layer and head)",
+        "config": {"workload": cfg["workload"], "batch": stack.B, "context": stack.C,
+                   "attended_tokens": stack.L, "layers": n_layers, "n_q_heads": stack.Hq,
+                   "n_kv_heads": stack.H, "head_dim": 128, "equiv_bits": kvq.kvq_equiv_bits(stack.model),
+                   "graph": not args.no_graph},
+        "packed_kv_gbps": step_bytes / (ms * 1e-3) / 1e9,
+        "packed_kv_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "step_alg_bytes": step_bytes,
+        "attention_only_ms_per_step": ms_attn,
+        "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "decode_kernel (kvq_decode_attn)",
+                     "avg_launch_us": sum(durs) / n_layers * 1e3,
+                     "alg_bytes_per_launch": sum(dbytes) / n_layers},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_pack(cfg, args):
+    """Prefill pack of 32768 bf16 tokens per layer for all 32 layers; source GB/s."""
+    import torch
+    import synth
+    import layer_wise_mixed_kvq_amd as kvq
+    dev = torch.device("cuda:0")
+    B, H, T = cfg["batch"], cfg["n_kv_heads"], cfg["context"]
+    model = kvq.Model(cfg["pairs"], cfg["n_q_heads"], H)
+    maxp = T // 32
+    bt = torch.arange(B * maxp, dtype=torch.int32, device=dev).view(B, maxp)
+    seq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    caches, ks, vs = [], [], []
+    log("[bench] generating 32 layers of bf16 sources ...")
+    for l in range(len(cfg["pairs"])):
+        caches.append(kvq.LayerCache(model, l, B, maxp, block_table=bt, device=dev))
+        cm = synth.outlier_mult(cfg["seed"], l, H, cfg["n_outliers"])
+        ks.append(synth.fill(cfg["seed"], synth.KIND_K, l, B, T, H, chan_mult=cm, device=dev))
+        vs.append(synth.fill(cfg["seed"], synth.KIND_V, l, B, T, H, device=dev))
+    torch.cuda.synchronize()
+
+    def step():
+        for l in range(len(caches)):
+            kvq.kvq_pack(model, l, caches[l], ks[l], vs[l], seq)
+
+    g = capture(step)
+    ms, wall = time_graph(g, args.steps, args.warmup)
+    src_bytes = 2 * B * T * H * 128 * 2 * len(caches)
+    page_bytes = sum(B * maxp * H * 512 * (kb + vb + 2) for kb, vb in cfg["pairs"])
+    durs = per_launch_durations(lambda l: kvq.kvq_pack(model, l, caches[l], ks[l], vs[l], seq), len(caches),
+                                args.roofline_reps)
+    achieved = (src_bytes + page_bytes) / (sum(durs) * 1e-3) / 1e9
+    rec = {
+        "metric": "mixed-precision KV prefill pack source GB/s (% HBM peak), 1 GPU",
+        "value": src_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s (bf16 source)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16-in, int2/4/8 codes", "data": "synthetic",
+        "config": {"workload": cfg["workload"], "tokens": T, "layers": len(caches)},
+        "total_gbps": (src_bytes + page_bytes) / (ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "pack_kernel (kvq_pack)",
+                     "avg_launch_us": sum(durs) / len(durs) * 1e3},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

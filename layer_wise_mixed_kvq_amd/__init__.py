@@ -1,0 +1,197 @@
+"""Layer-wise mixed-precision KV-cache quantization on MI355X (gfx950).
+
+A thin binding over the C ABI in ``include/kvq.h`` (``libkvq.so``): the functions below
+carry the C names, check tensor shapes and dtypes, and pass raw device pointers plus the
+current HIP stream.  Every step of the path runs in the library's kernels; PyTorch only
+provides device memory and streams.
+
+    model = Model([(4, 8)] * 3 + [(4, 2)] * 24 + [(2, 2)] * 4 + [(4, 8)], n_q_heads=32, n_kv_heads=8)
+    cache = LayerCache(model, layer, batch, max_pages)         # one per layer
+    kvq_pack(model, layer, cache, k_src, v_src, seq_len)        # prefill quantize-on-write
+    kvq_append(model, layer, cache, k_new, v_new, pos)          # decode quantize-on-write
+    out, lse = kvq_decode_attn(model, layer, cache, q, seq_len, max_seq_len)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+from . import _native
+from ._native import KVQ_BF16, KVQ_F32, KvqError, KvqLayerCache, KvqModel, check, lib
+
+HEAD_DIM = 128
+GROUP = 32
+
+__all__ = ["Model", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn",
+           "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_head_page_bytes",
+           "kvq_page_bytes", "kvq_equiv_bits", "kvq_format_version", "lib"]
+
+
+class Model:
+    """Per-layer (key bits, value bits) table plus the attention shape (kvq_model)."""
+
+    def __init__(self, pairs: Sequence[tuple[int, int]], n_q_heads: int, n_kv_heads: int,
+                 head_dim: int = HEAD_DIM):
+        self.pairs = [(int(k), int(v)) for k, v in pairs]
+        n = len(self.pairs)
+        self._kb = (ctypes.c_uint8 * max(n, 1))(*[k for k, _ in self.pairs])
+        self._vb = (ctypes.c_uint8 * max(n, 1))(*[v for _, v in self.pairs])
+        self.c = KvqModel(n, n_q_heads, n_kv_heads, head_dim,
+                          ctypes.cast(self._kb, ctypes.POINTER(ctypes.c_uint8)),
+                          ctypes.cast(self._vb, ctypes.POINTER(ctypes.c_uint8)))
+        self.n_layers, self.n_q_heads, self.n_kv_heads, self.head_dim = n, n_q_heads, n_kv_heads, head_dim
+
+    @property
+    def G(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    def validate(self) -> None:
+        check(lib().kvq_validate_model(ctypes.byref(self.c)), "kvq_validate_model")
+
+
+def kvq_format_version() -> int:
+    return int(lib().kvq_format_version())
+
+
+def kvq_head_page_bytes(k_bits: int, v_bits: int) -> int:
+    return int(lib().kvq_head_page_bytes(k_bits, v_bits))
+
+
+def kvq_page_bytes(model: Model, layer: int) -> int:
+    return int(lib().kvq_page_bytes(ctypes.byref(model.c), layer))
+
+
+def kvq_equiv_bits(model: Model) -> float:
+    return float(lib().kvq_equiv_bits(ctypes.byref(model.c)))
+
+
+class LayerCache:
+    """Device buffers of one layer (kvq_layer_cache).
+
+    pages       uint8 [n_pages][n_kv_heads][head page bytes of this layer's pair]
+    resid_k/v   bfloat16 [batch][n_kv_heads][32][128]
+    block_table int32 [batch][max_pages]; pass one tensor to every layer to share it.
+    """
+
+    def __init__(self, model: Model, layer: int, batch: int, max_pages: int,
+                 n_pages: Optional[int] = None, block_table=None, device="cuda"):
+        import torch
+        kb, vb = model.pairs[layer]
+        self.layer = layer
+        self.batch, self.max_pages = batch, max_pages
+        self.n_pages = batch * max_pages if n_pages is None else n_pages
+        hp = kvq_head_page_bytes(kb, vb)
+        self.pages = torch.zeros((self.n_pages, model.n_kv_heads, hp), dtype=torch.uint8, device=device)
+        self.resid_k = torch.zeros((batch, model.n_kv_heads, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        self.resid_v = torch.zeros_like(self.resid_k)
+        if block_table is None:
+            block_table = torch.arange(batch * max_pages, dtype=torch.int32, device=device).view(batch, max_pages)
+        assert block_table.dtype == torch.int32 and tuple(block_table.shape) == (batch, max_pages)
+        assert block_table.is_contiguous()
+        self.block_table = block_table
+
+    def c_struct(self) -> KvqLayerCache:
+        return KvqLayerCache(self.pages.data_ptr(), self.n_pages, self.resid_k.data_ptr(),
+                             self.resid_v.data_ptr(), self.block_table.data_ptr(), self.batch,
+                             self.max_pages)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KVQ_BF16
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    raise TypeError(f"expected bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def kvq_pack(model: Model, layer: int, cache: LayerCache, k_src, v_src, seq_len, stream=None) -> None:
+    """Prefill quantize-on-write: k_src, v_src [batch][max_tokens][n_kv_heads][128]."""
+    import torch
+    for t, n in ((k_src, "k_src"), (v_src, "v_src"), (seq_len, "seq_len")):
+        _dev(t, n)
+    if k_src.shape != v_src.shape or k_src.dtype != v_src.dtype or k_src.dim() != 4:
+        raise ValueError("k_src and v_src must have the same [batch][tokens][heads][128] shape and dtype")
+    if k_src.shape[0] != cache.batch or k_src.shape[2] != model.n_kv_heads or k_src.shape[3] != HEAD_DIM:
+        raise ValueError(f"source shape {tuple(k_src.shape)} does not match the model and cache")
+    if seq_len.dtype != torch.int32 or seq_len.numel() != cache.batch:
+        raise ValueError("seq_len must be int32 [batch]")
+    cs = cache.c_struct()
+    check(lib().kvq_pack(ctypes.byref(model.c), layer, ctypes.byref(cs), _dtype_code(k_src),
+                         k_src.data_ptr(), v_src.data_ptr(), k_src.shape[1], seq_len.data_ptr(),
+                         _stream(stream)), "kvq_pack")
+
+
+def kvq_append(model: Model, layer: int, cache: LayerCache, k_new, v_new, pos, stream=None) -> None:
+    """Decode-time quantize-on-write of one bf16 token per sequence ([batch][n_kv_heads][128])."""
+    import torch
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (pos, "pos")):
+        _dev(t, n)
+    shape = (cache.batch, model.n_kv_heads, HEAD_DIM)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new / v_new must be {shape}")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("k_new / v_new must be bfloat16")
+    if pos.dtype != torch.int32 or pos.numel() != cache.batch:
+        raise ValueError("pos must be int32 [batch]")
+    cs = cache.c_struct()
+    check(lib().kvq_append(ctypes.byref(model.c), layer, ctypes.byref(cs), k_new.data_ptr(),
+                           v_new.data_ptr(), pos.data_ptr(), _stream(stream)), "kvq_append")
+
+
+def kvq_decode_workspace_bytes(model: Model, batch: int, max_seq_len: int, pages_per_split: int = 0) -> int:
+    n = int(lib().kvq_decode_workspace_bytes(ctypes.byref(model.c), batch, max_seq_len, pages_per_split))
+    if n == 0:
+        raise KvqError(_native.KVQ_ERR_INVALID_ARG, "kvq_decode_workspace_bytes")
+    return n
+
+
+def kvq_workspace_init(workspace, stream=None) -> None:
+    _dev(workspace, "workspace")
+    check(lib().kvq_workspace_init(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "kvq_workspace_init")
+
+
+def new_workspace(model: Model, batch: int, max_seq_len: int, pages_per_split: int = 0, device="cuda"):
+    """A zeroed workspace tensor for kvq_decode_attn."""
+    import torch
+    n = kvq_decode_workspace_bytes(model, batch, max_seq_len, pages_per_split)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def kvq_decode_attn(model: Model, layer: int, cache: LayerCache, q, seq_len, max_seq_len: int,
+                    pages_per_split: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """Single-token decode attention; q is [batch][n_q_heads][128] (bf16 or fp32).
+    Returns (out fp32 [batch][n_q_heads][128], lse fp32 [batch][n_q_heads])."""
+    import torch
+    _dev(q, "q")
+    _dev(seq_len, "seq_len")
+    if tuple(q.shape) != (cache.batch, model.n_q_heads, HEAD_DIM):
+        raise ValueError(f"q must be [{cache.batch}][{model.n_q_heads}][128]")
+    if seq_len.dtype != torch.int32 or seq_len.numel() != cache.batch:
+        raise ValueError("seq_len must be int32 [batch]")
+    if out is None:
+        out = torch.empty((cache.batch, model.n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((cache.batch, model.n_q_heads), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(model, cache.batch, max_seq_len, pages_per_split, q.device)
+    cs = cache.c_struct()
+    check(lib().kvq_decode_attn(ctypes.byref(model.c), layer, ctypes.byref(cs), _dtype_code(q),
+                                q.data_ptr(), seq_len.data_ptr(), max_seq_len, pages_per_split,
+                                out.data_ptr(), lse.data_ptr() if lse is not False else None,
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "kvq_decode_attn")
+    return out, lse

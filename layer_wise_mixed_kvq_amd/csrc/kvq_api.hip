@@ -1,0 +1,202 @@
+// kvq_api.hip -- the C ABI declared in include/kvq.h: host-side validation, split planning
+// and workspace sizing, then one kernel launch per call on the caller's stream.
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+int decode_max_g();
+}
+
+namespace {
+
+bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvq_status check_model(const kvq_model *m)
+{
+    if (!m || !m->k_bits || !m->v_bits) return KVQ_ERR_INVALID_ARG;
+    if (m->n_layers <= 0 || m->n_q_heads <= 0 || m->n_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
+    if (m->head_dim != KVQ_HEAD_DIM) return KVQ_ERR_UNSUPPORTED;
+    if (m->n_q_heads % m->n_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+    if (m->n_q_heads / m->n_kv_heads > kvq::decode_max_g()) return KVQ_ERR_UNSUPPORTED;
+    if (m->n_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+    for (int l = 0; l < m->n_layers; ++l)
+        if (!valid_bits(m->k_bits[l]) || !valid_bits(m->v_bits[l])) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+kvq_status check_layer(const kvq_model *m, int32_t layer, const kvq_layer_cache *c)
+{
+    kvq_status s = check_model(m);
+    if (s != KVQ_OK) return s;
+    if (layer < 0 || layer >= m->n_layers) return KVQ_ERR_INVALID_ARG;
+    if (!c || !c->pages || !c->resid_k || !c->resid_v || !c->block_table) return KVQ_ERR_INVALID_ARG;
+    if (c->batch <= 0 || c->batch > 65535 || c->max_pages <= 0 || c->n_pages <= 0) return KVQ_ERR_INVALID_ARG;
+    if (c->n_pages > (int64_t)INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    if (!aligned16(c->pages) || !aligned16(c->resid_k) || !aligned16(c->resid_v)) return KVQ_ERR_ALIGNMENT;
+    return KVQ_OK;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+int n_splits_for(int max_seq_len, int pps) { return (max_seq_len / KVQ_GROUP + pps - 1) / pps + 1; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_str(kvq_status s)
+{
+    switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_ALIGNMENT: return "KVQ_ERR_ALIGNMENT";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+    }
+    return "KVQ_ERR_UNKNOWN";
+}
+
+int32_t kvq_format_version(void) { return KVQ_FORMAT_VERSION; }
+
+size_t kvq_head_page_bytes(int32_t k_bits, int32_t v_bits)
+{
+    if (!valid_bits(k_bits) || !valid_bits(v_bits)) return 0;
+    return static_cast<size_t>(kvq::head_page_bytes(k_bits, v_bits));
+}
+
+size_t kvq_page_bytes(const kvq_model *model, int32_t layer)
+{
+    if (check_model(model) != KVQ_OK || layer < 0 || layer >= model->n_layers) return 0;
+    return static_cast<size_t>(model->n_kv_heads) *
+           kvq_head_page_bytes(model->k_bits[layer], model->v_bits[layer]);
+}
+
+double kvq_equiv_bits(const kvq_model *model)
+{
+    if (check_model(model) != KVQ_OK) return -1.0;
+    long long sum = 0;
+    for (int l = 0; l < model->n_layers; ++l) sum += model->k_bits[l] + model->v_bits[l];
+    return static_cast<double>(sum) / (2.0 * model->n_layers);
+}
+
+kvq_status kvq_validate_model(const kvq_model *model) { return check_model(model); }
+
+kvq_status kvq_pack(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                    kvq_dtype src_dtype, const void *k_src, const void *v_src, int32_t max_tokens,
+                    const int32_t *seq_len, void *stream)
+{
+    kvq_status s = check_layer(model, layer, cache);
+    if (s != KVQ_OK) return s;
+    if (!k_src || !v_src || !seq_len || max_tokens < 0) return KVQ_ERR_INVALID_ARG;
+    if (src_dtype != KVQ_BF16 && src_dtype != KVQ_F32) return KVQ_ERR_UNSUPPORTED;
+    if (!aligned16(k_src) || !aligned16(v_src)) return KVQ_ERR_ALIGNMENT;
+    if ((max_tokens + KVQ_GROUP - 1) / KVQ_GROUP > 2147483647) return KVQ_ERR_UNSUPPORTED;
+    if (max_tokens == 0) return KVQ_OK;
+    kvq::PackParams p;
+    p.k_src = k_src;
+    p.v_src = v_src;
+    p.seq_len = seq_len;
+    p.block_table = cache->block_table;
+    p.pages = cache->pages;
+    p.resid_k = cache->resid_k;
+    p.resid_v = cache->resid_v;
+    p.n_pages = cache->n_pages;
+    p.H = model->n_kv_heads;
+    p.batch = cache->batch;
+    p.max_tokens = max_tokens;
+    p.max_pages = cache->max_pages;
+    return hip_status(kvq::launch_pack(model->k_bits[layer], model->v_bits[layer], p,
+                                       src_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_append(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                      const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, void *stream)
+{
+    kvq_status s = check_layer(model, layer, cache);
+    if (s != KVQ_OK) return s;
+    if (!k_new || !v_new || !pos) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
+    kvq::AppendParams p;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.pos = pos;
+    p.block_table = cache->block_table;
+    p.pages = cache->pages;
+    p.resid_k = cache->resid_k;
+    p.resid_v = cache->resid_v;
+    p.n_pages = cache->n_pages;
+    p.H = model->n_kv_heads;
+    p.batch = cache->batch;
+    p.max_pages = cache->max_pages;
+    return hip_status(kvq::launch_append(model->k_bits[layer], model->v_bits[layer], p,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_model *model, int32_t batch, int32_t max_seq_len,
+                                  int32_t pages_per_split)
+{
+    if (check_model(model) != KVQ_OK || batch <= 0 || max_seq_len < 0 || pages_per_split < 0) return 0;
+    const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
+    const int pps = pages_per_split > 0 ? pages_per_split
+                                        : kvq::decode_default_pages_per_split(batch, H, max_seq_len / KVQ_GROUP);
+    return kvq::decode_workspace_layout(batch, H, G, n_splits_for(max_seq_len, pps)).bytes;
+}
+
+kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!workspace) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGNMENT;
+    return hip_status(kvq::launch_zero_fill(workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                           kvq_dtype q_dtype, const void *q, const int32_t *seq_len, int32_t max_seq_len,
+                           int32_t pages_per_split, float *out, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    kvq_status s = check_layer(model, layer, cache);
+    if (s != KVQ_OK) return s;
+    if (!q || !seq_len || !out || max_seq_len < 0 || pages_per_split < 0) return KVQ_ERR_INVALID_ARG;
+    if (q_dtype != KVQ_BF16 && q_dtype != KVQ_F32) return KVQ_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return KVQ_ERR_ALIGNMENT;
+    const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
+    const int pps = pages_per_split > 0 ? pages_per_split
+                                        : kvq::decode_default_pages_per_split(cache->batch, H, max_seq_len / KVQ_GROUP);
+    const int n_splits = n_splits_for(max_seq_len, pps);
+    if (n_splits > 65535) return KVQ_ERR_UNSUPPORTED;
+    const kvq::DecodeWorkspace ws = kvq::decode_workspace_layout(cache->batch, H, G, n_splits);
+    if (!workspace || workspace_bytes < ws.bytes) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGNMENT;
+    kvq::DecodeParams p;
+    char *w = static_cast<char *>(workspace);
+    p.q = q;
+    p.seq_len = seq_len;
+    p.block_table = cache->block_table;
+    p.pages = cache->pages;
+    p.resid_k = cache->resid_k;
+    p.resid_v = cache->resid_v;
+    p.out = out;
+    p.lse = lse;
+    p.part_o = reinterpret_cast<float *>(w + ws.part_o_off);
+    p.part_ml = reinterpret_cast<float *>(w + ws.part_ml_off);
+    p.counters = reinterpret_cast<int *>(w + ws.counters_off);
+    p.n_pages = cache->n_pages;
+    p.H = H;
+    p.G = G;
+    p.batch = cache->batch;
+    p.max_pages = cache->max_pages;
+    p.max_seq_len = max_seq_len;
+    p.pages_per_split = pps;
+    p.n_splits = n_splits;
+    return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], p,
+                                         q_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

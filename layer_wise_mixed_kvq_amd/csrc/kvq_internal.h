@@ -1,0 +1,72 @@
+// kvq_internal.h -- launch parameters and launchers behind the C ABI (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct PackParams {
+    const void *k_src;
+    const void *v_src;
+    const int32_t *seq_len;
+    const int32_t *block_table;
+    void *pages;
+    uint16_t *resid_k;
+    uint16_t *resid_v;
+    long long n_pages;
+    int H;
+    int batch;
+    int max_tokens;
+    int max_pages;
+};
+
+struct AppendParams {
+    const uint16_t *k_new;
+    const uint16_t *v_new;
+    const int32_t *pos;
+    const int32_t *block_table;
+    void *pages;
+    uint16_t *resid_k;
+    uint16_t *resid_v;
+    long long n_pages;
+    int H;
+    int batch;
+    int max_pages;
+};
+
+struct DecodeParams {
+    const void *q;
+    const int32_t *seq_len;
+    const int32_t *block_table;
+    const void *pages;
+    const uint16_t *resid_k;
+    const uint16_t *resid_v;
+    float *out;
+    float *lse;
+    float *part_o;        // [batch][H][n_splits][G][128]
+    float *part_ml;       // [batch][H][n_splits][G][2]  (running max in log2 units, sum)
+    int *counters;        // [batch][H]
+    long long n_pages;
+    int H;
+    int G;
+    int batch;
+    int max_pages;
+    int max_seq_len;
+    int pages_per_split;
+    int n_splits;         // page splits + 1 residual slot, per (b, h)
+};
+
+// Workspace layout of kvq_decode_attn for (batch, H, G, n_splits).
+struct DecodeWorkspace {
+    size_t part_o_off, part_ml_off, counters_off, bytes;
+};
+DecodeWorkspace decode_workspace_layout(int batch, int H, int G, int n_splits);
+int decode_default_pages_per_split(int batch, int H, int max_full_pages);
+
+hipError_t launch_pack(int kb, int vb, const PackParams &p, bool src_f32, hipStream_t s);
+hipError_t launch_append(int kb, int vb, const AppendParams &p, hipStream_t s);
+hipError_t launch_decode(int kb, int vb, const DecodeParams &p, bool q_f32, hipStream_t s);
+hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,279 @@
+// kvq_quant.hip -- quantize-on-write kernels for gfx950: prefill pack and decode-time
+// append (+ page flush).
+//
+// Method: keys are quantized per channel over 32-token groups, values per token over
+// 32-channel groups, each group with an fp16 scale and an fp16 zero (asymmetric min/max);
+// only newly generated tokens are quantized online, at their layer's pair.
+//   [Mixed-precision KV-cache quantization per-layer sensitivity (llms-explorer.com), Facts]
+//   [KVTuner OpenReview discussion (paperhub.cn/paper/zDwipF6h06), reply to reviewer 1,
+//    section 4; reply to reviewer 2, section 2; reply to reviewer 3, section 1]
+//
+// One workgroup of 256 threads quantizes one page of one KV head:
+//   1. the 32 x 128 K and V tiles are staged in LDS as binary32 (coalesced 8/16-byte
+//      loads, 16 threads per 256-byte token row);
+//   2. threads 0..127 each reduce one key channel over the 32 tokens, threads 128..255
+//      each reduce one (token, 32-channel group) of the values -- every thread owns exactly
+//      one group, so the min/max needs no cross-thread reduction;
+//   3. each thread encodes its own 32 values (binary32 subtract and correctly rounded
+//      divide, round half to even, clamp) and writes the codes as bytes to LDS;
+//   4. all 256 threads pack the code bytes into the bit layout and store whole dwords.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileStride = kHeadDim + 1;   // padded row: column walks hit distinct banks
+
+struct QuantSmem {
+    float k[kGroup * kTileStride];
+    float v[kGroup * kTileStride];
+    uint8_t kcode[kGroup * kHeadDim];        // [token][channel]
+    uint8_t vcode[kHeadDim * kGroup];        // [channel][token]
+};
+
+// Codec of one 32-value group held by one thread.  Strict IEEE binary32: the compiler
+// must not contract or reassociate anything in here.
+template <int BITS>
+__device__ __forceinline__ void quant_group(const float *x, int stride, uint32_t &sz_word,
+                                            uint8_t *codes, int code_stride)
+{
+#pragma clang fp contract(off)
+    float v[kGroup];
+    float mn, mx;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) v[i] = x[i * stride] + 0.0f;   // -0 -> +0
+    mn = v[0];
+    mx = v[0];
+#pragma unroll
+    for (int i = 1; i < kGroup; ++i) {
+        mn = v[i] < mn ? v[i] : mn;
+        mx = v[i] > mx ? v[i] : mx;
+    }
+    constexpr float levels = static_cast<float>((1 << BITS) - 1);
+    const float s32 = (mx - mn) / levels;
+    const uint16_t s16 = float_to_half_bits(s32);
+    const uint16_t z16 = float_to_half_bits(mn);
+    const float s = half_bits_to_float(s16);
+    const float z = half_bits_to_float(z16);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+        uint32_t code = 0;
+        if (s != 0.0f) {
+            const float q = (v[i] - z) / s;
+            float r = __builtin_rintf(q);
+            r = r < 0.0f ? 0.0f : r;
+            r = r > levels ? levels : r;
+            code = static_cast<uint32_t>(r);
+        }
+        codes[i * code_stride] = static_cast<uint8_t>(code);
+    }
+    sz_word = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
+}
+
+// Quantize the staged tiles of one page-head into `dst` (global).  All 256 threads call.
+template <int KB, int VB>
+__device__ void quantize_page(QuantSmem &sm, uint8_t *__restrict__ dst)
+{
+    using P = PageLayout<KB, VB>;
+    const int tid = threadIdx.x;
+    uint32_t *dst32 = reinterpret_cast<uint32_t *>(dst);
+    if (tid < kHeadDim) {
+        const int c = tid;
+        uint32_t w;
+        quant_group<KB>(&sm.k[c], kTileStride, w, &sm.kcode[c], kHeadDim);
+        dst32[P::kKSz / 4 + c] = w;
+    } else {
+        const int t = (tid - kHeadDim) & (kGroup - 1);
+        const int j = (tid - kHeadDim) >> 5;
+        uint32_t w;
+        quant_group<VB>(&sm.v[t * kTileStride + kGroup * j], 1, w, &sm.vcode[(kGroup * j) * kGroup + t],
+                        kGroup);
+        dst32[P::kVSz / 4 + kValueGroups * t + j] = w;
+    }
+    __syncthreads();
+    // K codes: dword d of the section holds 32/KB consecutive channels of one token row
+    constexpr int kPerWord = 32 / KB;
+    for (int d = tid; d < 128 * KB; d += kThreads) {
+        const int t = d / (4 * KB);
+        const int c0 = (d % (4 * KB)) * kPerWord;
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < kPerWord; ++i) w |= static_cast<uint32_t>(sm.kcode[t * kHeadDim + c0 + i]) << (i * KB);
+        dst32[P::kKCodes / 4 + d] = w;
+    }
+    // V codes: dword d holds 32/VB consecutive tokens of one channel row
+    constexpr int vPerWord = 32 / VB;
+    for (int d = tid; d < 128 * VB; d += kThreads) {
+        const int c = d / VB;
+        const int t0 = (d % VB) * vPerWord;
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < vPerWord; ++i) w |= static_cast<uint32_t>(sm.vcode[c * kGroup + t0 + i]) << (i * VB);
+        dst32[P::kVCodes / 4 + d] = w;
+    }
+}
+
+template <typename SrcT>
+struct Src;
+
+template <>
+struct Src<uint16_t> {   // bf16 bit patterns
+    static constexpr int kVec = 8;   // elements per 16-byte load
+    __device__ static void load(const uint16_t *p, float *out)
+    {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+    __device__ static uint16_t to_bf16(uint16_t x) { return x; }
+};
+
+template <>
+struct Src<float> {
+    static constexpr int kVec = 4;
+    __device__ static void load(const float *p, float *out)
+    {
+        const float4 f = *reinterpret_cast<const float4 *>(p);
+        out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
+    }
+    __device__ static uint16_t to_bf16(float x) { return float_to_bf16_bits(x); }
+};
+
+// Stage rows [0, ntok) of a 32-token tile whose token rows are `row_stride` elements apart.
+template <typename SrcT>
+__device__ void stage_tile(const SrcT *__restrict__ src, long long row_stride, float *tile)
+{
+    constexpr int V = Src<SrcT>::kVec;
+    constexpr int kChunks = kGroup * kHeadDim / V;
+    for (int i = threadIdx.x; i < kChunks; i += kThreads) {
+        const int t = i / (kHeadDim / V);
+        const int c = (i % (kHeadDim / V)) * V;
+        float x[V];
+        Src<SrcT>::load(src + t * row_stride + c, x);
+#pragma unroll
+        for (int e = 0; e < V; ++e) tile[t * kTileStride + c + e] = x[e];
+    }
+}
+
+// grid: (pages covering max_tokens, n_kv_heads, batch)
+template <int KB, int VB, typename SrcT>
+__global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
+{
+    __shared__ QuantSmem sm;
+    const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int L = p.seq_len[b];
+    if (L < 0 || L > p.max_tokens || L > kGroup * p.max_pages) return;
+    const int full = L / kGroup;
+    const SrcT *ks = static_cast<const SrcT *>(p.k_src);
+    const SrcT *vs = static_cast<const SrcT *>(p.v_src);
+    const long long row_stride = static_cast<long long>(p.H) * kHeadDim;
+    const long long base = ((static_cast<long long>(b) * p.max_tokens + static_cast<long long>(g) * kGroup) * p.H + h) *
+                           kHeadDim;
+    if (g < full) {
+        const int phys = p.block_table[static_cast<long long>(b) * p.max_pages + g];
+        if (phys < 0 || phys >= p.n_pages) return;
+        stage_tile<SrcT>(ks + base, row_stride, sm.k);
+        stage_tile<SrcT>(vs + base, row_stride, sm.v);
+        __syncthreads();
+        uint8_t *dst = static_cast<uint8_t *>(p.pages) +
+                       (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
+        quantize_page<KB, VB>(sm, dst);
+    } else if (g == full) {
+        // trailing L mod 32 tokens -> bf16 residual slots 0 .. L mod 32 - 1
+        const int nres = L - full * kGroup;
+        const long long rbase = (static_cast<long long>(b) * p.H + h) * kGroup * kHeadDim;
+        for (int i = threadIdx.x; i < nres * kHeadDim; i += kThreads) {
+            const int t = i / kHeadDim, c = i % kHeadDim;
+            const long long si = base + t * row_stride + c;
+            p.resid_k[rbase + i] = Src<SrcT>::to_bf16(ks[si]);
+            p.resid_v[rbase + i] = Src<SrcT>::to_bf16(vs[si]);
+            (void)c;
+        }
+    }
+}
+
+// grid: (n_kv_heads, batch)
+template <int KB, int VB>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p)
+{
+    __shared__ QuantSmem sm;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int pos = p.pos[b];
+    if (pos < 0 || pos >= kGroup * p.max_pages) return;
+    const int slot = pos % kGroup;
+    const long long nb = (static_cast<long long>(b) * p.H + h) * kHeadDim;
+    const long long rbase = (static_cast<long long>(b) * p.H + h) * kGroup * kHeadDim;
+    const int tid = threadIdx.x;
+    // the new token into its residual slot (threads 0..127: K, 128..255: V)
+    if (tid < kHeadDim)
+        p.resid_k[rbase + slot * kHeadDim + tid] = p.k_new[nb + tid];
+    else
+        p.resid_v[rbase + slot * kHeadDim + tid - kHeadDim] = p.v_new[nb + tid - kHeadDim];
+    if (slot != kGroup - 1) return;
+    // the group is complete: quantize the 31 older residual tokens plus the new one
+    const int phys = p.block_table[static_cast<long long>(b) * p.max_pages + pos / kGroup];
+    if (phys < 0 || phys >= p.n_pages) return;
+    for (int i = tid; i < kGroup * kHeadDim; i += kThreads) {
+        const int t = i / kHeadDim, c = i % kHeadDim;
+        const uint16_t kb16 = (t == kGroup - 1) ? p.k_new[nb + c] : p.resid_k[rbase + i];
+        const uint16_t vb16 = (t == kGroup - 1) ? p.v_new[nb + c] : p.resid_v[rbase + i];
+        sm.k[t * kTileStride + c] = bf16_bits_to_float(kb16);
+        sm.v[t * kTileStride + c] = bf16_bits_to_float(vb16);
+    }
+    __syncthreads();
+    uint8_t *dst = static_cast<uint8_t *>(p.pages) + (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
+    quantize_page<KB, VB>(sm, dst);
+}
+
+template <int KB, int VB>
+hipError_t launch_pack_t(const PackParams &p, bool src_f32, hipStream_t s)
+{
+    const int gx = (p.max_tokens + kGroup - 1) / kGroup;
+    if (gx == 0) return hipSuccess;
+    dim3 grid(gx, p.H, p.batch);
+    if (src_f32)
+        hipLaunchKernelGGL((pack_kernel<KB, VB, float>), grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((pack_kernel<KB, VB, uint16_t>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int KB, int VB>
+hipError_t launch_append_t(const AppendParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL((append_kernel<KB, VB>), dim3(p.H, p.batch), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define KVQ_DISPATCH_PAIR(KBV, VBV, CALL) \
+    if (kb == KBV && vb == VBV) return CALL<KBV, VBV>
+
+hipError_t launch_pack(int kb, int vb, const PackParams &p, bool src_f32, hipStream_t s)
+{
+#define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_pack_t<KBV, VBV>(p, src_f32, s)
+    KVQ_P(2, 2); KVQ_P(2, 4); KVQ_P(2, 8);
+    KVQ_P(4, 2); KVQ_P(4, 4); KVQ_P(4, 8);
+    KVQ_P(8, 2); KVQ_P(8, 4); KVQ_P(8, 8);
+#undef KVQ_P
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_append(int kb, int vb, const AppendParams &p, hipStream_t s)
+{
+#define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_append_t<KBV, VBV>(p, s)
+    KVQ_P(2, 2); KVQ_P(2, 4); KVQ_P(2, 8);
+    KVQ_P(4, 2); KVQ_P(4, 4); KVQ_P(4, 8);
+    KVQ_P(8, 2); KVQ_P(8, 4); KVQ_P(8, 8);
+#undef KVQ_P
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -40,7 +40,10 @@
  *   A layer's pool is [physical page][KV head][head_page], head_page = 512*(kb+vb+2) bytes:
  *     +0              K codes, token-major: row t (16*kb bytes), channel c at bit c*kb
  *     +512*kb         K scale/zero: 128 x u32, word c = s16 | z16 << 16
- *     +512*kb+512     V codes, channel-major: row c (4*vb bytes), token t at bit t*vb
+ *     +512*kb+512     V codes: 64 chunks of 8*vb bytes; chunk 16*q + r holds tokens
+ *                     8q..8q+7 of channels r, r+16, ..., r+112; inside it, with
+ *                     i = t%8, j = i%4, k = 4*(c/16) + j, n = 16/vb, the code of
+ *                     (t, c) is at bit 32*(k/n) + 16*(i/4) + vb*(k%n)
  *     +512*(kb+vb)+512 V scale/zero: 128 x u32, word 4*t + j (channels 32j..32j+31)
  *   Codes are little-endian, LSB-first.  block_table[b][i] names the physical page that
  *   holds tokens 32i..32i+31 of sequence b; one block table serves every layer, each
@@ -151,7 +154,7 @@ kvq_status kvq_append(const kvq_model *model, int32_t layer, const kvq_layer_cac
                       void *stream);
 
 /* Workspace bytes kvq_decode_attn needs for this batch, longest sequence and split size
- * (pages_per_split 0 = the library's choice). */
+ * (pages_per_split 0 = the library's choice, values above 256 act as 256). */
 size_t kvq_decode_workspace_bytes(const kvq_model *model, int32_t batch, int32_t max_seq_len,
                                   int32_t pages_per_split);
 
@@ -169,8 +172,8 @@ kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, void *str
  *   lse:      device fp32 [batch][n_q_heads], natural-log log-sum-exp of the scaled
  *             scores, or NULL
  *   A sequence of length 0 yields out = 0 and lse = -inf.
- *   pages_per_split: pages per split-K work item (0 = the library's choice); the result
- *   depends on it only through floating-point rounding.
+ *   pages_per_split: pages per split-K work item (0 = the library's choice; values above
+ *   256 act as 256); the result depends on it only through floating-point rounding.
  *   workspace: device memory of at least kvq_decode_workspace_bytes(...) bytes, zeroed once
  *   before first use (kvq_workspace_init).  Calls that share a workspace must not overlap. */
 kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,

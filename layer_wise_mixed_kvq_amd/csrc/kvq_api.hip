@@ -45,6 +45,15 @@ kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_
 
 int n_splits_for(int max_seq_len, int pps) { return (max_seq_len / KVQ_GROUP + pps - 1) / pps + 1; }
 
+// pages per split-K work item: the caller's value (at most 256: a workgroup's four waves
+// hold at most 64 page ids each), or the library's choice for 0
+int plan_pages_per_split(int requested, int batch, int H, int max_seq_len)
+{
+    if (requested > 256) return 256;
+    if (requested > 0) return requested;
+    return kvq::decode_default_pages_per_split(batch, H, max_seq_len / KVQ_GROUP);
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,8 +152,7 @@ size_t kvq_decode_workspace_bytes(const kvq_model *model, int32_t batch, int32_t
 {
     if (check_model(model) != KVQ_OK || batch <= 0 || max_seq_len < 0 || pages_per_split < 0) return 0;
     const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
-    const int pps = pages_per_split > 0 ? pages_per_split
-                                        : kvq::decode_default_pages_per_split(batch, H, max_seq_len / KVQ_GROUP);
+    const int pps = plan_pages_per_split(pages_per_split, batch, H, max_seq_len);
     return kvq::decode_workspace_layout(batch, H, G, n_splits_for(max_seq_len, pps)).bytes;
 }
 
@@ -167,8 +175,7 @@ kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_laye
     if (!aligned16(q) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return KVQ_ERR_ALIGNMENT;
     const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
-    const int pps = pages_per_split > 0 ? pages_per_split
-                                        : kvq::decode_default_pages_per_split(cache->batch, H, max_seq_len / KVQ_GROUP);
+    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, max_seq_len);
     const int n_splits = n_splits_for(max_seq_len, pps);
     if (n_splits > 65535) return KVQ_ERR_UNSUPPORTED;
     const kvq::DecodeWorkspace ws = kvq::decode_workspace_layout(cache->batch, H, G, n_splits);

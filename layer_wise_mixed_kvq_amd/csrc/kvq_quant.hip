@@ -103,14 +103,23 @@ __device__ void quantize_page(QuantSmem &sm, uint8_t *__restrict__ dst)
         for (int i = 0; i < kPerWord; ++i) w |= static_cast<uint32_t>(sm.kcode[t * kHeadDim + c0 + i]) << (i * KB);
         dst32[P::kKCodes / 4 + d] = w;
     }
-    // V codes: dword d holds 32/VB consecutive tokens of one channel row
-    constexpr int vPerWord = 32 / VB;
+    // V codes: 64 chunks of 2*VB words; chunk 16q + r holds tokens 8q..8q+7 of channels
+    // r, r+16, ..., r+112.  Word dw of a chunk holds, in each 16-bit half hh, the codes of
+    // k = dw*n .. dw*n + n-1 (n = 16/VB), k = 4*(c/16) + (t%4), token t = 8q + (t%4) + 4hh.
+    constexpr int n = 16 / VB;
     for (int d = tid; d < 128 * VB; d += kThreads) {
-        const int c = d / VB;
-        const int t0 = (d % VB) * vPerWord;
+        const int u = d / (2 * VB), dw = d % (2 * VB);
+        const int q = u >> 4, r = u & 15;
         uint32_t w = 0;
 #pragma unroll
-        for (int i = 0; i < vPerWord; ++i) w |= static_cast<uint32_t>(sm.vcode[c * kGroup + t0 + i]) << (i * VB);
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int kk = 0; kk < n; ++kk) {
+                const int k = dw * n + kk;
+                const int t = 8 * q + (k & 3) + 4 * hh, c = 16 * (k >> 2) + r;
+                w |= static_cast<uint32_t>(sm.vcode[c * kGroup + t]) << (16 * hh + VB * kk);
+            }
+        }
         dst32[P::kVCodes / 4 + d] = w;
     }
 }

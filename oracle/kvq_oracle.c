@@ -176,8 +176,8 @@ int orc_quant_group(const float *x, int stride, int bits,
 /*                       c sits at bit c*kb of row t (LSB-first, little-endian bytes)    */
 /*   offset 512*kb       K scale/zero: 128 words of 32 bits; word c = s16 | z16 << 16,   */
 /*                       the group of channel c over the page's 32 tokens                */
-/*   offset 512*kb+512   V codes, channel-major: 128 rows of 4*vb bytes; channel c,      */
-/*                       token t sits at bit t*vb of row c (LSB-first)                   */
+/*   offset 512*kb+512   V codes, 64 chunks of 8*vb bytes; see vcode_bit() for the bit   */
+/*                       of (token t, channel c)                                         */
 /*   offset 512*(kb+vb)+512  V scale/zero: 32 tokens x 4 groups of 32-bit words;         */
 /*                       word 4*t + j = s16 | z16 << 16 for channels 32j .. 32j+31       */
 /*   total 512*(kb+vb+2) bytes                                                           */
@@ -192,6 +192,34 @@ static size_t off_kcodes(int kb, int vb) { (void)kb; (void)vb; return 0; }
 static size_t off_ksz(int kb, int vb) { (void)vb; return (size_t)512 * kb; }
 static size_t off_vcodes(int kb, int vb) { (void)vb; return (size_t)512 * kb + 512; }
 static size_t off_vsz(int kb, int vb) { return (size_t)512 * (kb + vb) + 512; }
+
+/* Bit offset of the value code of (token t, channel c) inside the V code section.
+ * The section is 64 chunks of 8*vb bytes.  Chunk 16*q + r holds the 64 codes of tokens
+ * 8q .. 8q+7 and channels r, r+16, ..., r+112.  Inside a chunk, with i = t mod 8,
+ * j = i mod 4, hh = i / 4, nb = c / 16, k = 4*nb + j and n = 16 / vb codes per 16-bit
+ * half-word, the code sits at bit 32*(k / n) + 16*hh + vb*(k mod n).
+ * (Each 16-bit half of a 32-bit word then holds codes of consecutive k for one half of
+ * the token octet, so one shift and one mask extract a pair of codes of one channel for
+ * tokens 8q+j and 8q+j+4.) */
+static size_t vcode_bit(int t, int c, int vb)
+{
+    int q = t / 8, i = t % 8, r = c % 16, nb = c / 16;
+    int j = i % 4, hh = i / 4;
+    int k = 4 * nb + j;
+    int n = 16 / vb;
+    size_t chunk_bits = (size_t)(16 * q + r) * 8 * vb * 8;
+    return chunk_bits + 32 * (size_t)(k / n) + 16 * (size_t)hh + (size_t)vb * (k % n);
+}
+
+static void put_code_at(uint8_t *base, size_t bit, unsigned code)
+{
+    base[bit / 8] |= (uint8_t)(code << (bit % 8));
+}
+
+static unsigned get_code_at(const uint8_t *base, size_t bit, int bits)
+{
+    return (base[bit / 8] >> (bit % 8)) & ((1u << bits) - 1u);
+}
 
 static void put_code(uint8_t *row, int idx, int bits, unsigned code)
 {
@@ -235,7 +263,7 @@ int orc_pack_page(const float *k, const float *v, int tok_stride, int kb, int vb
         for (int j = 0; j < ORC_D / ORC_G; ++j) {
             orc_quant_group(v + (size_t)t * tok_stride + 32 * j, 1, vb, &s16, &z16, codes);
             for (int i = 0; i < ORC_G; ++i)
-                put_code(dst + off_vcodes(kb, vb) + (size_t)(32 * j + i) * 4 * vb, t, vb, codes[i]);
+                put_code_at(dst + off_vcodes(kb, vb), vcode_bit(t, 32 * j + i, vb), codes[i]);
             put_u32(dst + off_vsz(kb, vb) + 4 * (size_t)(4 * t + j),
                     (uint32_t)s16 | (uint32_t)z16 << 16);
         }
@@ -262,7 +290,7 @@ int orc_dequant_page(const uint8_t *src, int kb, int vb, double *k, double *v)
             uint32_t w = get_u32(src + off_vsz(kb, vb) + 4 * (size_t)(4 * t + c / 32));
             double s = orc_f16_to_f32((uint16_t)(w & 0xffffu));
             double z = orc_f16_to_f32((uint16_t)(w >> 16));
-            unsigned code = get_code(src + off_vcodes(kb, vb) + (size_t)c * 4 * vb, t, vb);
+            unsigned code = get_code_at(src + off_vcodes(kb, vb), vcode_bit(t, c, vb), vb);
             v[t * ORC_D + c] = (double)code * s + z;
         }
     }

@@ -287,9 +287,17 @@ def test_packed_bytes_hand_derived(orc):
     assert all(kc[t].tolist() == [0xE4] * 32 for t in range(2, 32))
     ksz = page[1024:1536].view(np.uint32)
     assert np.all(ksz == 0x3C00)            # s = 1.0 (0x3C00) in the low half, z = +0 above
-    vc = page[1536:2560].reshape(128, 8)    # channel-major: row c = 32 tokens x 2 bits
-    assert vc[0].tolist() == [0xFF] * 8     # channel 0 is 3 for every token
-    assert vc[1].tolist() == [0] * 8
+    # V codes, 2-bit: channels 0, 32, 64, 96 (r = 0, nb = 0, 2, 4, 6) have code 3 for every
+    # token.  They sit in chunks 0, 16, 32, 48 (one per token octet, 16 bytes each); with
+    # n = 8 codes per half-word, k = 4*nb + j -> word nb/2, bits 2j (tokens 8q..8q+3) and
+    # 16 + 2j (tokens 8q+4..8q+7): words 0..3 of those chunks are 0x00FF00FF.
+    vc = page[1536:2560]
+    want = np.zeros(1024, dtype=np.uint8)
+    for q in range(4):
+        for w in range(4):
+            want[16 * q * 16 + 4 * w + 0] = 0xFF
+            want[16 * q * 16 + 4 * w + 2] = 0xFF
+    assert np.array_equal(vc, want)
     vsz = page[2560:3072].view(np.uint32).reshape(32, 4)
     assert np.all(vsz == 0x3C00)
     # 4-bit keys: nibble order inside a byte is LSB-first
@@ -299,13 +307,21 @@ def test_packed_bytes_hand_derived(orc):
     page = orc.pack_page(k4, v, 4, 2)
     row5 = page[5 * 64:(5 + 1) * 64]
     assert row5[0] == 0x21 and row5[1] == 0x0F and not row5[2:].any()
-    # 8-bit values: row c holds 32 token bytes in token order
+    # 8-bit values: (token 7, channel 3): q = 0, r = 3 -> chunk 3 (64 bytes at offset 192);
+    # i = 7 -> j = 3, half 1; k = 3 -> word 1, bit 16 + 8 = 24 -> byte 4 + 3 = 7: offset 199.
+    # Channel 31 (r = 15, nb = 1) is 255 for every token: chunks 15, 31, 47, 63, k = 4..7
+    # -> words 2 and 3 of each chunk are all ones.
     v8 = np.zeros((32, 128), dtype=np.float32)
     v8[:, 31] = 255.0                       # channel 31 pins s = 1 for group 0 of every token
     v8[7, 3] = 200.0
     page = orc.pack_page(k4, v8, 4, 8)
-    vc8 = page[4 * 512 + 512: 4 * 512 + 512 + 4096].reshape(128, 32)
-    assert vc8[3, 7] == 200 and vc8[3].sum() == 200 and np.all(vc8[31] == 255)
+    vc8 = page[4 * 512 + 512: 4 * 512 + 512 + 4096]
+    want = np.zeros(4096, dtype=np.uint8)
+    want[199] = 200
+    for q in range(4):
+        base = (16 * q + 15) * 64
+        want[base + 8: base + 16] = 255
+    assert np.array_equal(vc8, want)
 
 
 @pytest.mark.parametrize("kb,vb", PAIRS)

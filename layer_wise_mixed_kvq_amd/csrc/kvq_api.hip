@@ -43,7 +43,12 @@ kvq_status check_layer(const kvq_model *m, int32_t layer, const kvq_layer_cache 
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-int n_splits_for(int max_seq_len, int pps) { return (max_seq_len / KVQ_GROUP + pps - 1) / pps + 1; }
+// page splits of the longest sequence (at least one workgroup per (sequence, KV head))
+int n_splits_for(int max_seq_len, int pps)
+{
+    const int n = (max_seq_len / KVQ_GROUP + pps - 1) / pps;
+    return n > 0 ? n : 1;
+}
 
 // pages per split-K work item: the caller's value (at most 256: a workgroup's four waves
 // hold at most 64 page ids each), or the library's choice for 0

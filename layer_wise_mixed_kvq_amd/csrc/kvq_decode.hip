@@ -14,8 +14,10 @@
 // the raw integer codes:
 //   score(t) = sum_c q_c (k_tc s_c + z_c) = sum_c (q_c s_c) k_tc + sum_c q_c z_c
 //   out(c)   = sum_t p_t (v_tc s_tg + z_tg) = sum_t (p_t s_tg) v_tc + sum_t p_t z_tg
-// Codes are unpacked with one shift, one mask-and-or and one packed subtract per pair into
-// exact fp16 integers (OR into 1024.0, subtract 1024).  The folded operands (q s and p s) are split into
+// Codes are unpacked with a shift, a bit-insert into 1024.0 and a packed subtract per pair
+// into exact normal fp16 integers: the matrix cores accumulate subnormal fp16 operands
+// several bits less accurately, which the scores (a small difference of two large sums)
+// and the value sums do not tolerate.  The folded operands (q s and p s) are split into
 // fp16 hi + lo parts (22 significant bits) and both parts are fed to the MFMA with the same
 // code operand.  Both are scaled by powers of two so their largest values sit just below
 // 2^15: q s per page (from the page's largest key scale), p s per wave (from the largest
@@ -23,11 +25,11 @@
 // the matrix cores accumulate at full binary32 accuracy.
 //
 // Work decomposition.  One workgroup of four waves per (split, KV head, sequence).  Split
-// s < n_ps covers pages [s*P, min((s+1)*P, full)), each wave taking every fourth page;
-// split n_ps (when L mod 32 > 0) attends over the bf16 residual.  A wave keeps its own
-// online-softmax state; the four are merged in LDS, and every split writes (m, l, o[128])
-// per query head to the workspace.  The last split of a (sequence, KV head) to finish --
-// a device-scope counter -- merges the splits:
+// s covers pages [s*P, min((s+1)*P, full)), each wave taking every fourth page.  A wave
+// keeps its own online-softmax state; the four are merged in LDS, and every split writes
+// (m, l, o[128]) per query head to the workspace.  The last split of a (sequence, KV head)
+// to finish -- a device-scope counter -- attends over the L mod 32 bf16 residual tokens
+// itself and merges everything:
 //   m = max m_s, l = sum 2^(m_s - m) l_s, out = sum 2^(m_s - m) o_s / l, lse = (m + log2 l) ln 2
 // and resets the counter for the next call.  Scores are in log2 units (q carries
 // log2(e)/sqrt(128)).
@@ -85,31 +87,51 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ float row_max(float v)   // over the 16 lanes of a lane group
+// Reductions over the 16 lanes of a lane group with DPP (no LDS round trip): xor 1 and
+// xor 2 via quad permutes, then row_half_mirror and row_mirror fold the quads and the two
+// halves; every lane of the group ends with the result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
 {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
-    return v;
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+
+__device__ __forceinline__ float fdpp1(float v) { return __uint_as_float(dpp<kQuadXor1>(__float_as_uint(v))); }
+__device__ __forceinline__ float fdpp2(float v) { return __uint_as_float(dpp<kQuadXor2>(__float_as_uint(v))); }
+__device__ __forceinline__ float fdpp3(float v) { return __uint_as_float(dpp<kRowHalfMirror>(__float_as_uint(v))); }
+__device__ __forceinline__ float fdpp4(float v) { return __uint_as_float(dpp<kRowMirror>(__float_as_uint(v))); }
+
+__device__ __forceinline__ float row_max(float v)
+{
+    v = fmaxf(v, fdpp1(v));
+    v = fmaxf(v, fdpp2(v));
+    v = fmaxf(v, fdpp3(v));
+    return fmaxf(v, fdpp4(v));
 }
 
 __device__ __forceinline__ float row_sum(float v)
 {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    return v;
+    v += fdpp1(v);
+    v += fdpp2(v);
+    v += fdpp3(v);
+    return v + fdpp4(v);
 }
 
 __device__ __forceinline__ uint32_t row_max_u32(uint32_t v)
 {
-    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 1)));
-    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 2)));
-    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 4)));
-    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 8)));
-    return v;
+    v = max(v, dpp<kQuadXor1>(v));
+    v = max(v, dpp<kQuadXor2>(v));
+    v = max(v, dpp<kRowHalfMirror>(v));
+    return max(v, dpp<kRowMirror>(v));
+}
+
+// maximum over the whole wave of a value that is already uniform within each lane group
+__device__ __forceinline__ uint32_t groups_max_u32(uint32_t v)
+{
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
 }
 
 template <typename QT>
@@ -125,14 +147,26 @@ __device__ __forceinline__ float load_q<float>(const void *q, long long i)
     return static_cast<const float *>(q)[i];
 }
 
-// Pair j (0..3) of operand `op` from a lane's packed codes, as exact small integers in the
-// normal fp16 range: with n = 16/BITS codes per 16-bit half, k = 4*op + j sits in word
-// k / n at shift BITS*(k % n) in both halves; OR into 1024.0 (0x6400, whose spacing is 1),
-// then subtract 1024 with one packed add.  The matrix cores keep full binary32 accuracy
-// only for normal fp16 inputs (subnormal operands lose about four bits in the
-// accumulation).
+// 1024.0 in both fp16 halves, opaque to the optimizer so that the unpack below stays one
+// bit-field insert (v_bfi_b32) instead of a constant-folded and + or.  The empty asm emits
+// no instruction: the register is written by an ordinary compiler-generated move.
+__device__ __forceinline__ uint32_t fp16x2_1024()
+{
+    uint32_t m = 0x64006400u;
+    __asm__ volatile("" : "+v"(m));
+    return m;
+}
+
+// Pair j (0..3) of operand `op` from a lane's packed codes, as exact normal fp16 integers:
+// with n = 16/BITS codes per 16-bit half, k = 4*op + j sits in word k / n at shift
+// BITS*(k % n) in both halves.  The code bits are inserted into 1024.0 (0x6400, spacing 1)
+// and one packed subtract removes the 1024.  The matrix cores keep full binary32 accuracy
+// only for normal fp16 inputs: subnormal operands lose about four bits in the accumulation.
+// No inline asm writes a register here: the hazard recognizer does not see registers an
+// asm statement writes, and a register that is dead in an MFMA result can be reused while
+// that MFMA is still in flight, which has to wait until the MFMA retires.
 template <int BITS>
-__device__ __forceinline__ uint4 unpack_operand_normal(const uint32_t *w, int op)
+__device__ __forceinline__ uint4 unpack_codes(const uint32_t *w, int op, uint32_t magic)
 {
     constexpr int n = 16 / BITS;
     constexpr uint32_t M = ((1u << BITS) - 1u) * 0x00010001u;
@@ -141,8 +175,8 @@ __device__ __forceinline__ uint4 unpack_operand_normal(const uint32_t *w, int op
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int k = 4 * op + j;
-        const uint32_t x = ((w[k / n] >> (BITS * (k % n))) & M) | 0x64006400u;
-        r[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x) + bias);
+        const uint32_t y = ((w[k / n] >> (BITS * (k % n))) & M) | (magic & ~M);
+        r[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, y) + bias);
     }
     return make_uint4(r[0], r[1], r[2], r[3]);
 }
@@ -158,11 +192,11 @@ __device__ __forceinline__ int key_pair_channel(int jj, int j)
 
 template <int GS>
 struct WaveLds {
-    uint32_t qp[2][4 * GS + 1][64];      // (q s) hi / lo pairs: [part][head, + zero row][pair]
-    float p[32][4 * GS];                 // softmax weights of the page: [token][head]
-    uint32_t pp[2][4][4 * GS + 1][16];   // (p s) hi / lo pairs: [part][value group][head][pair]
+    alignas(16) uint32_t qp[2][4 * GS + 1][64];      // (q s) hi / lo pairs: [part][head, + zero row][pair]
+    alignas(16) uint32_t pp[2][4][4 * GS + 1][16];   // (p s) hi / lo pairs: [part][value group][head][pair]
+    float p[32][4 * GS];                             // softmax weights of the page: [token][head]
     float alpha[4 * GS];
-    float bv[4][4 * GS];                 // value zero terms at the end: [group][head]
+    float bv[4][4 * GS];                             // value zero terms at the end: [group][head]
 };
 
 template <int GS>
@@ -173,20 +207,31 @@ struct MergeLds {
 };
 
 template <int GS>
+struct ResidualLds {
+    float k[kGroup][kHeadDim];
+    float v[kGroup][kHeadDim];
+    float s[4 * GS][kGroup];
+    float o[4 * GS][kHeadDim];
+    float m[4 * GS];
+    float l[4 * GS];
+};
+
+template <int GS>
 struct DecodeSmem {
-    float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128) * 2^eq[h], |.| in [1, 2) per head
-    int eq[4 * GS];
+    float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128)
+    int eq[4 * GS];               // per head: |qs * 2^eq| in [1, 2)
     union {
         WaveLds<GS> w[kWaves];
         MergeLds<GS> merge;
-        struct {
-            float k[kGroup][kHeadDim];
-            float v[kGroup][kHeadDim];
-            float s[4 * GS][kGroup];
-        } res;
+        ResidualLds<GS> res;
     } u;
     int last;
 };
+
+__device__ __forceinline__ uint4 lds_read16(const uint32_t *p)
+{
+    return *reinterpret_cast<const uint4 *>(__builtin_assume_aligned(p, 16));
+}
 
 // Split partials cross workgroups (and XCDs, whose L2s are not coherent with each other),
 // so they are written and read with device-scope relaxed atomics (sc1 stores / loads,
@@ -208,41 +253,18 @@ __device__ __forceinline__ void wait_stores()
 }
 
 // ------------------------------------------------------------------------------------
-// split-K combine (last split of a (sequence, KV head))
-// ------------------------------------------------------------------------------------
-__device__ void combine_splits(const DecodeParams &p, long long bh, int expected, int G, float *out_bh, float *lse_bh)
-{
-    const long long slot0 = bh * p.n_splits;
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
-        const int g = idx / kHeadDim, c = idx % kHeadDim;
-        float m = -INFINITY;
-        for (int s = 0; s < expected; ++s) m = fmaxf(m, load_dev(&p.part_ml[((slot0 + s) * G + g) * 2]));
-        float l = 0.0f, o = 0.0f;
-        for (int s = 0; s < expected; ++s) {
-            const float ms = load_dev(&p.part_ml[((slot0 + s) * G + g) * 2]);
-            const float ls = load_dev(&p.part_ml[((slot0 + s) * G + g) * 2 + 1]);
-            const float w = exp2f(ms - m);
-            l = fmaf(w, ls, l);
-            o = fmaf(w, load_dev(&p.part_o[((slot0 + s) * G + g) * kHeadDim + c]), o);
-        }
-        out_bh[g * kHeadDim + c] = o / l;
-        if (lse_bh && c == 0) lse_bh[g] = (m + log2f(l)) * kLn2;
-    }
-}
-
-// ------------------------------------------------------------------------------------
-// residual split: up to 31 bf16 tokens, plain VALU
+// residual tokens (at most 31, bf16), plain VALU, into LDS: (m, l, o) per head
 // ------------------------------------------------------------------------------------
 template <int GS>
-__device__ void residual_split(const DecodeParams &p, DecodeSmem<GS> &sm, long long bh, int nres, int G,
-                               long long slot)
+__device__ void residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, long long bh, int nres, int G)
 {
+    ResidualLds<GS> &R = sm.u.res;
     const int tid = threadIdx.x;
     const uint16_t *rk = p.resid_k + bh * kGroup * kHeadDim;
     const uint16_t *rv = p.resid_v + bh * kGroup * kHeadDim;
     for (int i = tid; i < nres * kHeadDim; i += kThreads) {
-        sm.u.res.k[i / kHeadDim][i % kHeadDim] = bf16_bits_to_float(rk[i]);
-        sm.u.res.v[i / kHeadDim][i % kHeadDim] = bf16_bits_to_float(rv[i]);
+        R.k[i / kHeadDim][i % kHeadDim] = bf16_bits_to_float(rk[i]);
+        R.v[i / kHeadDim][i % kHeadDim] = bf16_bits_to_float(rv[i]);
     }
     __syncthreads();
     // scores: thread (t, part) covers channels 16*part .. 16*part+15 of token t
@@ -252,41 +274,40 @@ __device__ void residual_split(const DecodeParams &p, DecodeSmem<GS> &sm, long l
             float s = 0.0f;
             if (t < nres) {
 #pragma unroll
-                for (int x = 0; x < 16; ++x) s = fmaf(sm.qs[h][16 * part + x], sm.u.res.k[t][16 * part + x], s);
+                for (int x = 0; x < 16; ++x) s = fmaf(sm.qs[h][16 * part + x], R.k[t][16 * part + x], s);
             }
             s += __shfl_xor(s, 1);
             s += __shfl_xor(s, 2);
             s += __shfl_xor(s, 4);
-            if (part == 0) sm.u.res.s[h][t] = t < nres ? ldexpf(s, -sm.eq[h]) : -INFINITY;
+            if (part == 0) R.s[h][t] = t < nres ? s : -INFINITY;
         }
     }
     __syncthreads();
-    float *part_ml = p.part_ml + slot * G * 2;
     if (tid < G) {
         const int h = tid;
         float m = -INFINITY;
-        for (int t = 0; t < nres; ++t) m = fmaxf(m, sm.u.res.s[h][t]);
+        for (int t = 0; t < nres; ++t) m = fmaxf(m, R.s[h][t]);
         float l = 0.0f;
         for (int t = 0; t < kGroup; ++t) {
-            const float e = t < nres ? exp2f(sm.u.res.s[h][t] - m) : 0.0f;
-            sm.u.res.s[h][t] = e;
+            const float e = t < nres ? exp2f(R.s[h][t] - m) : 0.0f;
+            R.s[h][t] = e;
             l += e;
         }
-        store_dev(&part_ml[2 * h], m);
-        store_dev(&part_ml[2 * h + 1], l);
+        R.m[h] = m;
+        R.l[h] = l;
     }
     __syncthreads();
-    float *part_o = p.part_o + slot * G * kHeadDim;
     for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
         const int h = idx / kHeadDim, c = idx % kHeadDim;
         float o = 0.0f;
-        for (int t = 0; t < nres; ++t) o = fmaf(sm.u.res.s[h][t], sm.u.res.v[t][c], o);
-        store_dev(&part_o[idx], o);
+        for (int t = 0; t < nres; ++t) o = fmaf(R.s[h][t], R.v[t][c], o);
+        R.o[h][c] = o;
     }
+    __syncthreads();
 }
 
 // ------------------------------------------------------------------------------------
-// the page splits
+// the page work of one wave
 // ------------------------------------------------------------------------------------
 template <int KB, int VB>
 struct PageRegs {
@@ -339,6 +360,7 @@ template <int KB, int VB, int GS, typename QT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 {
     using PL = PageLayout<KB, VB>;
+    constexpr int HS = 4 * GS;                 // head slots
     __shared__ DecodeSmem<GS> sm;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
@@ -360,64 +382,90 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const int full = L / kGroup, nres = L % kGroup;
     const int P = p.pages_per_split;
     const int n_ps = (full + P - 1) / P;
-    const int expected = n_ps + (nres > 0 ? 1 : 0);
-    if (split >= expected) return;
-    const long long slot = bh * p.n_splits + split;
+    if (split >= (n_ps > 0 ? n_ps : 1)) return;
 
-    // q, scaled to log2 units and normalized per head to |q~| in [1, 2)
-    for (int i = tid; i < G * kHeadDim; i += kThreads)
-        sm.qs[i / kHeadDim][i % kHeadDim] = load_q<QT>(p.q, bh * G * kHeadDim + i) * kScoreScale;
-    __syncthreads();
-    if (tid < G) {
-        float mx = 0.0f;
-        for (int c = 0; c < kHeadDim; ++c) mx = fmaxf(mx, fabsf(sm.qs[tid][c]));
-        int e = 0;
-        if (mx > 0.0f) frexpf(mx, &e);
-        sm.eq[tid] = 1 - e;
+    const int wave = tid >> 6, lane = tid & 63;
+    // ---- prologue: q, this wave's block-table ids and its first page are all requested
+    // before anything waits on them ------------------------------------------------------
+    constexpr int kQPer = (HS * kHeadDim + kThreads - 1) / kThreads;
+    float qv[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+        const int i = tid + k * kThreads;
+        qv[k] = i < G * kHeadDim ? load_q<QT>(p.q, bh * G * kHeadDim + i) * kScoreScale : 0.0f;
+    }
+    const int pg_begin = split * P + wave;
+    const int pg_end = min(full, (split + 1) * P);
+    const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
+    int my_phys = 0;
+    if (lane < n_my) my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + pg_begin + kWaves * lane];
+    // lane roles in the page loop
+    const int a = lane >> 4, r16 = lane & 15;
+    const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
+    const int ch0 = 32 * kq + key_pair_channel<KB>(kjj, kj);
+    const int ch1 = ch0 + 16 / KB;
+    const int t0 = 8 * (r16 >> 2) + (r16 & 3), t1 = t0 + 4;   // value pair this lane folds (group a)
+    const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
+    auto page_base = [&](int j, bool &ok) -> const uint8_t * {
+        const int phys = __builtin_amdgcn_readlane(my_phys, j);
+        ok = phys >= 0 && phys < p.n_pages;
+        return pool + (static_cast<long long>(ok ? phys : 0) * p.H + h) * PL::kBytes;
+    };
+    bool bad_page = false;
+    PageRegs<KB, VB> cur, nxt;
+    if (n_my > 0) {
+        bool ok;
+        const uint8_t *base = page_base(0, ok);
+        bad_page |= !ok;
+        load_page<KB, VB>(cur, base, lane, ch0, ch1, t0, t1);
+    }
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < G * kHeadDim) sm.qs[i / kHeadDim][i % kHeadDim] = qv[k];
     }
     __syncthreads();
-    for (int i = tid; i < G * kHeadDim; i += kThreads)
-        sm.qs[i / kHeadDim][i % kHeadDim] = ldexpf(sm.qs[i / kHeadDim][i % kHeadDim], sm.eq[i / kHeadDim]);
+    // per-head normalization exponent: |q * 2^eq| in [1, 2); wave w reduces heads w, w+4, ...
+    for (int hh = wave; hh < G; hh += kWaves) {
+        float mx = fmaxf(fabsf(sm.qs[hh][lane]), fabsf(sm.qs[hh][lane + 64]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if (lane == 0) {
+            int e = 0;
+            if (mx > 0.0f) frexpf(mx, &e);
+            sm.eq[hh] = 1 - e;
+        }
+    }
     __syncthreads();
 
-    if (split == n_ps) {
-        residual_split<GS>(p, sm, bh, nres, G, slot);
-    } else {
-        const int wave = tid >> 6, lane = tid & 63;
-        const int a = lane >> 4, r16 = lane & 15;
+    const long long slot0 = bh * p.n_splits;
+    if (n_ps > 0) {
         WaveLds<GS> &W = sm.u.w[wave];
-        // zero rows (A operands of rows whose head is >= G)
-        for (int i = lane; i < 64; i += 64) {
-            W.qp[0][4 * GS][i] = 0u;
-            W.qp[1][4 * GS][i] = 0u;
+        for (int i = lane; i < 64; i += 64) {      // zero rows: A operands of absent heads
+            W.qp[0][HS][i] = 0u;
+            W.qp[1][HS][i] = 0u;
+            W.pp[0][i / 16][HS][i % 16] = 0u;
+            W.pp[1][i / 16][HS][i % 16] = 0u;
         }
-        for (int i = lane; i < 4 * 16; i += 64) {
-            W.pp[0][i / 16][4 * GS][i % 16] = 0u;
-            W.pp[1][i / 16][4 * GS][i % 16] = 0u;
-        }
-        // lane roles
         const int hr = 4 * (r16 & 3) + (r16 >> 2);             // head of A row r16
-        const int arow = hr < G ? hr : 4 * GS;                  // zero row when absent
-        const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
-        const int ch0 = 32 * kq + key_pair_channel<KB>(kjj, kj);
-        const int ch1 = ch0 + 16 / KB;
-        const int t0 = 8 * (r16 >> 2) + (r16 & 3), t1 = t0 + 4;   // value pair this lane folds (group a)
-        float qw[4 * GS][2];                                      // q~ of the folded key pair, every head
+        const int arow = hr < G ? hr : HS;                      // zero row when absent
+        float qw[HS][2];                                        // q~ of the folded key pair, every head
+        float qb[GS][8];                                        // q~ of the zero-term channels
+        float inv_eq[GS];                                       // 2^-eq of the lane's heads
 #pragma unroll
-        for (int hh = 0; hh < 4 * GS; ++hh) {
-            qw[hh][0] = hh < G ? sm.qs[hh][ch0] : 0.0f;
-            qw[hh][1] = hh < G ? sm.qs[hh][ch1] : 0.0f;
+        for (int hh = 0; hh < HS; ++hh) {
+            qw[hh][0] = hh < G ? ldexpf(sm.qs[hh][ch0], sm.eq[hh]) : 0.0f;
+            qw[hh][1] = hh < G ? ldexpf(sm.qs[hh][ch1], sm.eq[hh]) : 0.0f;
         }
-        float qb[GS][8];                                          // q~ of the zero-term channels
-        float eqs[GS];
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
             const int hh = 4 * i + a;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) qb[i][x] = hh < G ? sm.qs[hh][8 * r16 + x] : 0.0f;
-            eqs[i] = hh < G ? static_cast<float>(sm.eq[hh]) : 0.0f;
+            for (int x = 0; x < 8; ++x) qb[i][x] = hh < G ? ldexpf(sm.qs[hh][8 * r16 + x], sm.eq[hh]) : 0.0f;
+            inv_eq[i] = hh < G ? ldexpf(1.0f, -sm.eq[hh]) : 0.0f;
         }
 
+        const uint32_t magic = fp16x2_1024();
         float4_t acc[8];
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -427,66 +475,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             m_run[i] = -INFINITY;
             l_part[i] = 0.0f;
         }
-        float zb[4 * GS];
+        float zb[HS];
 #pragma unroll
-        for (int hh = 0; hh < 4 * GS; ++hh) zb[hh] = 0.0f;
-        // The value accumulators hold sum_t (p s 2^ev) v: ev keeps the folded weights in the
-        // normal fp16 range (|p s 2^ev| < 2^15); it only decreases, rescaling acc when it does.
+        for (int hh = 0; hh < HS; ++hh) zb[hh] = 0.0f;
+        // The value accumulators hold sum_t (p s 2^ev) v: ev keeps the folded
+        // weights in the normal fp16 range (|p s 2^ev| < 2^15); it only decreases, rescaling
+        // acc when it does.
         int ev = 127;
-        bool bad_page = false;
 
-        const int pg_begin = split * P + wave;
-        const int pg_end = min(full, (split + 1) * P);
-        const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
-        // physical ids of this wave's pages (pg_begin + 4j, j < 64), one per lane
-        const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
-        int my_phys = 0;
-        if (lane < n_my) my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + pg_begin + kWaves * lane];
-        auto page_base = [&](int j, bool &ok) -> const uint8_t * {
-            const int phys = __builtin_amdgcn_readlane(my_phys, j);
-            ok = phys >= 0 && phys < p.n_pages;
-            return pool + (static_cast<long long>(ok ? phys : 0) * p.H + h) * PL::kBytes;
-        };
-
-        PageRegs<KB, VB> cur, nxt;
-        if (n_my > 0) {
-            bool ok;
-            const uint8_t *base = page_base(0, ok);
-            bad_page |= !ok;
-            load_page<KB, VB>(cur, base, lane, ch0, ch1, t0, t1);
-        }
-        for (int j = 0; j < n_my; ++j) {
-            if (j + 1 < n_my) {
-                bool ok;
-                const uint8_t *base = page_base(j + 1, ok);
-                bad_page |= !ok;
-                load_page<KB, VB>(nxt, base, lane, ch0, ch1, t0, t1);
-            }
+        auto process_page = [&](const PageRegs<KB, VB> &cur) {
             // ---- page exponent: |q~ s 2^E| < 2^15 for every channel ---------------
             uint32_t smax = 0;
 #pragma unroll
             for (int x = 0; x < 8; ++x) smax = max(smax, cur.kszb[x] & 0x7FFFu);
             smax = row_max_u32(smax);
             int E = 0;
-            {
-                const float sm_f = half_bits_to_float(smax);
-                if (sm_f > 0.0f) {
-                    int e;
-                    frexpf(sm_f, &e);
-                    E = 14 - e;
-                }
+            if (smax != 0u) {
+                int e;
+                frexpf(half_bits_to_float(smax), &e);
+                E = 14 - e;
             }
-            // ---- fold key scales into q: two channels x every head, hi/lo ------------
+            // ---- fold key scales into q: two channels x every head slot, hi/lo ---------
             {
                 const float s0 = ldexpf(half_bits_to_float(cur.kszw[0] & 0xFFFFu), E);
                 const float s1 = ldexpf(half_bits_to_float(cur.kszw[1] & 0xFFFFu), E);
 #pragma unroll
-                for (int hh = 0; hh < 4 * GS; ++hh) {
-                    if (hh < G) {
-                        const uint32_t hi = split_hi(qw[hh][0] * s0, qw[hh][1] * s1);
-                        W.qp[0][hh][lane] = hi;
-                        W.qp[1][hh][lane] = split_lo(qw[hh][0], s0, qw[hh][1], s1, hi);
-                    }
+                for (int hh = 0; hh < HS; ++hh) {
+                    const uint32_t hi = split_hi(qw[hh][0] * s0, qw[hh][1] * s1);
+                    W.qp[0][hh][lane] = hi;
+                    W.qp[1][hh][lane] = split_lo(qw[hh][0], s0, qw[hh][1], s1, hi);
                 }
             }
             // ---- key zero terms: sum_c q~_c z_c per head, lane group a holds heads a+4i
@@ -500,25 +517,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             }
             wave_lds_sync();
             // ---- scores on MFMA ------------------------------------------------------
-            float4_t sacc[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+            float4_t sacc[2];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const uint4 ahi = *reinterpret_cast<const uint4 *>(&W.qp[0][arow][16 * a + 4 * jj]);
-                const uint4 alo = *reinterpret_cast<const uint4 *>(&W.qp[1][arow][16 * a + 4 * jj]);
+                const uint4 ahi = lds_read16(&W.qp[0][arow][16 * a + 4 * jj]);
+                const uint4 alo = lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
-                    const uint4 bk = unpack_operand_normal<KB>(cur.kc[blk], jj);
-                    sacc[blk] = mfma(ahi, bk, sacc[blk]);
+                    const uint4 bk = unpack_codes<KB>(cur.kc[blk], jj, magic);
+                    sacc[blk] = mfma(ahi, bk, jj == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : sacc[blk]);
                     sacc[blk] = mfma(alo, bk, sacc[blk]);
                 }
             }
             // ---- online softmax ------------------------------------------------------
             float s2[2][GS];
             bool grow = false;
+            const float sce = ldexpf(1.0f, -E);
 #pragma unroll
             for (int i = 0; i < GS; ++i) {
-                const float sc = ldexpf(1.0f, -E) * exp2f(-eqs[i]);
-                const float bc = bias[i] * exp2f(-eqs[i]);
+                const float sc = sce * inv_eq[i];
+                const float bc = bias[i] * inv_eq[i];
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
                     s2[blk][i] = fmaf(sacc[blk][i], sc, bc);
@@ -536,12 +554,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     l_part[i] *= alpha[i];
 #pragma unroll
                     for (int nb = 0; nb < 8; ++nb) acc[nb][i] *= alpha[i];
-                    if (r16 == 0 && 4 * i + a < G) W.alpha[4 * i + a] = alpha[i];
+                    if (r16 == 0) W.alpha[4 * i + a] = alpha[i];
                 }
                 wave_lds_sync();
 #pragma unroll
-                for (int hh = 0; hh < 4 * GS; ++hh)
-                    if (hh < G) zb[hh] *= W.alpha[hh];
+                for (int hh = 0; hh < HS; ++hh) zb[hh] *= W.alpha[hh];
             }
 #pragma unroll
             for (int i = 0; i < GS; ++i) {
@@ -549,16 +566,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 for (int blk = 0; blk < 2; ++blk) {
                     const float pv = __builtin_amdgcn_exp2f(s2[blk][i] - m_run[i]);
                     l_part[i] += pv;
-                    if (4 * i + a < G) W.p[16 * blk + r16][4 * i + a] = pv;
+                    W.p[16 * blk + r16][4 * i + a] = pv;
                 }
             }
-            wave_lds_sync();
             // ---- value-scale exponent of this page -----------------------------------
             {
                 uint32_t vmax = max(cur.vszw[0] & 0x7FFFu, cur.vszw[1] & 0x7FFFu);
-                vmax = row_max_u32(vmax);
-                vmax = max(vmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(vmax), 16)));
-                vmax = max(vmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(vmax), 32)));
+                vmax = groups_max_u32(row_max_u32(vmax));
                 if (vmax != 0u) {
                     int e;
                     frexpf(half_bits_to_float(vmax), &e);
@@ -571,37 +585,49 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     }
                 }
             }
-            // ---- fold value scales into p: two tokens x every head, hi/lo --------------
+            wave_lds_sync();
+            // ---- fold value scales into p: two tokens x every head slot, hi/lo ----------
             {
                 const float sv0 = ldexpf(half_bits_to_float(cur.vszw[0] & 0xFFFFu), ev);
                 const float sv1 = ldexpf(half_bits_to_float(cur.vszw[1] & 0xFFFFu), ev);
                 const float zv0 = half_bits_to_float(cur.vszw[0] >> 16);
                 const float zv1 = half_bits_to_float(cur.vszw[1] >> 16);
 #pragma unroll
-                for (int hh = 0; hh < 4 * GS; ++hh) {
-                    if (hh < G) {
-                        const float p0 = W.p[t0][hh], p1 = W.p[t1][hh];
-                        const uint32_t hi = split_hi(p0 * sv0, p1 * sv1);
-                        W.pp[0][a][hh][r16] = hi;
-                        W.pp[1][a][hh][r16] = split_lo(p0, sv0, p1, sv1, hi);
-                        zb[hh] = fmaf(p0, zv0, fmaf(p1, zv1, zb[hh]));
-                    }
+                for (int hh = 0; hh < HS; ++hh) {
+                    const float p0 = W.p[t0][hh], p1 = W.p[t1][hh];
+                    const uint32_t hi = split_hi(p0 * sv0, p1 * sv1);
+                    W.pp[0][a][hh][r16] = hi;
+                    W.pp[1][a][hh][r16] = split_lo(p0, sv0, p1, sv1, hi);
+                    zb[hh] = fmaf(p0, zv0, fmaf(p1, zv1, zb[hh]));
                 }
             }
             wave_lds_sync();
             // ---- values on MFMA ------------------------------------------------------
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint4 ahi = *reinterpret_cast<const uint4 *>(&W.pp[0][g][arow][4 * a]);
-                const uint4 alo = *reinterpret_cast<const uint4 *>(&W.pp[1][g][arow][4 * a]);
+                const uint4 ahi = lds_read16(&W.pp[0][g][arow][4 * a]);
+                const uint4 alo = lds_read16(&W.pp[1][g][arow][4 * a]);
 #pragma unroll
                 for (int nb = 2 * g; nb < 2 * g + 2; ++nb) {
-                    const uint4 bv = unpack_operand_normal<VB>(cur.vc, nb);
+                    const uint4 bv = unpack_codes<VB>(cur.vc, nb, magic);
                     acc[nb] = mfma(ahi, bv, acc[nb]);
                     acc[nb] = mfma(alo, bv, acc[nb]);
                 }
             }
-            cur = nxt;
+        };
+        // two page buffers in turn: page j+1 is in flight while page j is processed
+        auto prefetch = [&](PageRegs<KB, VB> &dst, int j) {
+            bool ok;
+            const uint8_t *base = page_base(j, ok);
+            bad_page |= !ok;
+            load_page<KB, VB>(dst, base, lane, ch0, ch1, t0, t1);
+        };
+        for (int j = 0; j < n_my; j += 2) {
+            if (j + 1 < n_my) prefetch(nxt, j + 1);
+            process_page(cur);
+            if (j + 1 >= n_my) break;
+            if (j + 2 < n_my) prefetch(cur, j + 2);
+            process_page(nxt);
         }
 
         // ---- this wave's state: l per head, value zero terms, unnormalized output -------
@@ -609,21 +635,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
         for (int i = 0; i < GS; ++i) lw[i] = row_sum(l_part[i]);
 #pragma unroll
-        for (int hh = 0; hh < 4 * GS; ++hh) {
-            if (hh < G) {
-                const float v = row_sum(zb[hh]);    // lanes of group a cover all 32 tokens once
-                if (r16 == 0) W.bv[a][hh] = v;
-            }
+        for (int hh = 0; hh < HS; ++hh) {
+            const float v = row_sum(zb[hh]);    // lanes of group a cover all 32 tokens once
+            if (r16 == 0) W.bv[a][hh] = v;
         }
         wave_lds_sync();
         float o_out[8][GS];
+        const float unscale = ldexpf(1.0f, -ev);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int i = 0; i < GS; ++i) {
-                const int hh = 4 * i + a;
-                o_out[nb][i] = hh < G ? fmaf(acc[nb][i], ldexpf(1.0f, -ev), W.bv[nb >> 1][hh]) : 0.0f;
-            }
+            for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(acc[nb][i], unscale, W.bv[nb >> 1][4 * i + a]);
         __syncthreads();     // every wave is done with its WaveLds: reuse the space to merge
         MergeLds<GS> &M = sm.u.merge;
 #pragma unroll
@@ -638,10 +660,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 }
             }
         }
-        __syncthreads();
-        float *part_o = p.part_o + slot * G * kHeadDim;
-        float *part_ml = p.part_ml + slot * G * 2;
         const bool bad = __syncthreads_or(bad_page);
+        float *part_o = p.part_o + (slot0 + split) * G * kHeadDim;
+        float *part_ml = p.part_ml + (slot0 + split) * G * 2;
         for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
             const int hh = idx / kHeadDim, c = idx % kHeadDim;
             float m = -INFINITY;
@@ -660,16 +681,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 store_dev(&part_ml[2 * hh + 1], bad ? NAN : l);
             }
         }
+        wait_stores();
+        __syncthreads();
+        if (tid == 0)
+            sm.last = __hip_atomic_fetch_add(p.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_ps - 1;
+        __syncthreads();
+        if (!sm.last) return;
     }
 
-    wait_stores();
-    __syncthreads();
-    if (tid == 0)
-        sm.last = __hip_atomic_fetch_add(p.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == expected - 1;
-    __syncthreads();
-    if (!sm.last) return;
-    combine_splits(p, bh, expected, G, out_bh, lse_bh);
-    if (tid == 0) __hip_atomic_store(p.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- last split of this (sequence, KV head): residual tokens, then merge everything
+    if (nres > 0) residual_tokens<GS>(p, sm, bh, nres, G);
+    const ResidualLds<GS> &R = sm.u.res;
+    for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
+        const int g = idx / kHeadDim, c = idx % kHeadDim;
+        float m = nres > 0 ? R.m[g] : -INFINITY;
+        for (int s = 0; s < n_ps; ++s) m = fmaxf(m, load_dev(&p.part_ml[((slot0 + s) * G + g) * 2]));
+        float l = 0.0f, o = 0.0f;
+        if (nres > 0) {
+            const float w = exp2f(R.m[g] - m);
+            l = w * R.l[g];
+            o = w * R.o[g][c];
+        }
+        for (int s = 0; s < n_ps; ++s) {
+            const float ms = load_dev(&p.part_ml[((slot0 + s) * G + g) * 2]);
+            const float ls = load_dev(&p.part_ml[((slot0 + s) * G + g) * 2 + 1]);
+            const float w = exp2f(ms - m);
+            l = fmaf(w, ls, l);
+            o = fmaf(w, load_dev(&p.part_o[((slot0 + s) * G + g) * kHeadDim + c]), o);
+        }
+        out_bh[g * kHeadDim + c] = o / l;
+        if (lse_bh && c == 0) lse_bh[g] = (m + log2f(l)) * kLn2;
+    }
+    if (n_ps > 0 && tid == 0) __hip_atomic_store(p.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words)
@@ -715,13 +758,14 @@ DecodeWorkspace decode_workspace_layout(int batch, int H, int G, int n_splits)
 
 int decode_default_pages_per_split(int batch, int H, int max_full_pages)
 {
-    // about 1024 workgroups of four waves for the longest sequences, at least four pages
-    // per wave, at most 128 pages per split
+    // about 512 workgroups of four waves for the longest sequences (two per CU resident at
+    // once), at least four pages per wave, at most 64 per wave (block-table ids are held
+    // one per lane)
     const long long work = static_cast<long long>(batch) * H * (max_full_pages > 0 ? max_full_pages : 1);
-    long long pps = (work + 1023) / 1024;
+    long long pps = (work + 511) / 512;
     pps = (pps + kWaves - 1) / kWaves * kWaves;
     if (pps < 4 * kWaves) pps = 4 * kWaves;
-    if (pps > 128) pps = 128;   // at most 32 pages per wave (block-table ids held one per lane)
+    if (pps > 256) pps = 256;
     return static_cast<int>(pps);
 }
 

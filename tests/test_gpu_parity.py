@@ -66,7 +66,7 @@ def test_config_single_layer_k8v4_fp32(kvq, orc):
 
 
 @pytest.mark.parametrize("kb,vb", PAIRS)
-@pytest.mark.parametrize("G", [1, 4, 7])
+@pytest.mark.parametrize("G", [1, 4, 7, 12, 16])
 def test_decode_parity(kvq, orc, kb, vb, G):
     c = Case(kb, vb, H=2, G=G, lens=[1, 31, 32, 33, 200, 517], seed=kb * 100 + vb * 10 + G)
     log(f"decode kb={kb} vb={vb} G={G}")

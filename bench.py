@@ -14,7 +14,9 @@ Inputs are seeded synthetic tensors (synth/), generated on the device; the timed
 starts with the packed cache resident in HBM.  The step is captured once as a HIP graph and
 replayed (no allocation or host work inside the timed region).
 
-Prints ONE JSON line.  Other workloads: --config qwen | pack | single.
+Prints ONE JSON line.  Other workloads: --config qwen | pack | single | copy (a plain
+streaming kernel of known size: the measured bandwidth ceiling, and the calibration of the
+HBM byte counters).
 """
 from __future__ import annotations
 
@@ -45,7 +47,29 @@ CONFIGS = {
     "pack": dict(workload="prefill pack, llama3.1-8b shape C3.25, 32768 tokens, batch 1 (32 layers)",
                  pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=1, context=32768, n_outliers=3,
                  seed=20250206),
+    "copy": dict(workload="streaming copy: 1 GiB int32 read + 1 GiB written (torch bitwise_not)"),
 }
+
+
+# sources the decode kernel is built from: a stored HBM-traffic measurement is reported only
+# while they are unchanged
+DECODE_SOURCES = ["layer_wise_mixed_kvq_amd/csrc/kvq_decode.hip", "layer_wise_mixed_kvq_amd/csrc/kvq_device.h",
+                  "layer_wise_mixed_kvq_amd/csrc/kvq_internal.h"]
+COPY_BYTES = 1 << 30
+
+
+def measured_traffic(config):
+    """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE measurement of
+    this workload, or None when there is none or the kernel changed since it was taken."""
+    from layer_wise_mixed_kvq_amd.profiling import source_hash
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash([os.path.join(ROOT, x) for x in DECODE_SOURCES]):
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def log(msg):
@@ -232,6 +256,8 @@ def main():
     cfg = CONFIGS[args.config]
     if args.config == "pack":
         return bench_pack(cfg, args)
+    if args.config == "copy":
+        return bench_copy(args)
 
     log(f"[bench] building {args.config} cache ...")
     t0 = time.perf_counter()
@@ -261,12 +287,18 @@ def main():
     ms_attn, _ = time_graph(g_attn, args.steps, 2)
     log(f"[bench] step {ms:.4f} ms (attention only {ms_attn:.4f} ms)")
 
-    # live per-launch durations of the dominant kernel (decode attention), every layer
+    # the dominant kernel (decode attention): its average launch duration is the
+    # attention-only step (one launch per layer, replayed as a graph on the stream the kernels
+    # run on, timed with events over the whole timed region) divided by the layer count;
+    # event pairs around single eager launches are reported beside it (they add a few us of
+    # marker overhead per launch)
     n_layers = len(cfg["pairs"])
-    durs = per_launch_durations(stack.decode_layer, n_layers, args.roofline_reps)
     dbytes = stack.decode_bytes()
-    achieved = sum(dbytes) / (sum(durs) * 1e-3) / 1e9
-    log(f"[bench] decode kernel avg {sum(durs) / n_layers * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
+    launch_us = ms_attn * 1e3 / n_layers
+    achieved = sum(dbytes) / (ms_attn * 1e-3) / 1e9
+    durs = per_launch_durations(stack.decode_layer, n_layers, args.roofline_reps)
+    log(f"[bench] decode kernel avg {launch_us:.2f} us/launch (graph), "
+        f"{sum(durs) / n_layers * 1e3:.2f} us (eager, event pairs); {achieved:.1f} GB/s")
 
     step_bytes = stack.alg_bytes(with_append)
     tokens_per_s = stack.B * 1000.0 / ms
@@ -302,9 +334,10 @@ def main():
         "attention_only_ms_per_step": ms_attn,
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
                      "kernel": "decode_kernel (kvq_decode_attn)",
-                     "avg_launch_us": sum(durs) / n_layers * 1e3,
+                     "avg_launch_us": launch_us,
+                     "avg_launch_us_eager_events": sum(durs) / n_layers * 1e3,
                      "alg_bytes_per_launch": sum(dbytes) / n_layers},
         "cpu_baseline": cpu,
     }
@@ -339,9 +372,10 @@ def bench_pack(cfg, args):
     ms, wall = time_graph(g, args.steps, args.warmup)
     src_bytes = 2 * B * T * H * 128 * 2 * len(caches)
     page_bytes = sum(B * maxp * H * 512 * (kb + vb + 2) for kb, vb in cfg["pairs"])
-    durs = per_launch_durations(lambda l: kvq.kvq_pack(model, l, caches[l], ks[l], vs[l], seq), len(caches),
-                                args.roofline_reps)
-    achieved = (src_bytes + page_bytes) / (sum(durs) * 1e-3) / 1e9
+    # average launch duration: the graph of one pack launch per layer, timed over the whole
+    # timed region, divided by the layer count
+    launch_us = ms * 1e3 / len(caches)
+    achieved = (src_bytes + page_bytes) / (ms * 1e-3) / 1e9
     rec = {
         "metric": "mixed-precision KV prefill pack source GB/s (% HBM peak), 1 GPU",
         "value": src_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s (bf16 source)", "n_gpus": 1,
@@ -351,9 +385,41 @@ def bench_pack(cfg, args):
         "total_gbps": (src_bytes + page_bytes) / (ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "pack_kernel (kvq_pack)",
-                     "avg_launch_us": sum(durs) / len(durs) * 1e3},
+                     "avg_launch_us": launch_us, "alg_bytes_per_launch": (src_bytes + page_bytes) / len(caches)},
         "cpu_baseline": None,
     }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_copy(args):
+    """A plain streaming kernel of known size (torch's elementwise bitwise_not over 1 GiB of
+    int32 into another 1 GiB): the bandwidth a simple kernel reaches on this GPU, and the
+    reference against which the HBM byte counters are scaled."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = COPY_BYTES // 4
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        torch.bitwise_not(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert int(dst[12345].item()) == ~12345
+    gbps = 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+    rec = {"metric": "streaming copy GB/s (read + write), 1 GPU", "value": gbps, "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+           "config": {"workload": CONFIGS["copy"]["workload"], "bytes_read": COPY_BYTES,
+                      "bytes_written": COPY_BYTES},
+           "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "torch bitwise_not"},
+           "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
 

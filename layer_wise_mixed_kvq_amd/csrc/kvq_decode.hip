@@ -207,23 +207,36 @@ struct MergeLds {
 };
 
 template <int GS>
-struct ResidualLds {
+struct ResidualLds {              // staging of the residual tokens
     float k[kGroup][kHeadDim];
     float v[kGroup][kHeadDim];
     float s[4 * GS][kGroup];
+};
+
+template <int GS>
+struct ResidualOut {              // (m, l, o) of the residual tokens, kept for the merge
     float o[4 * GS][kHeadDim];
     float m[4 * GS];
     float l[4 * GS];
+};
+
+// (m, l) of a chunk of split partials, staged for the final merge
+constexpr int kMergeChunk = 64;
+struct CombineLds {
+    float m[kMergeChunk][16];
+    float l[kMergeChunk][16];
 };
 
 template <int GS>
 struct DecodeSmem {
     float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128)
     int eq[4 * GS];               // per head: |qs * 2^eq| in [1, 2)
+    ResidualOut<GS> ro;
     union {
         WaveLds<GS> w[kWaves];
         MergeLds<GS> merge;
         ResidualLds<GS> res;
+        CombineLds comb;
     } u;
     int last;
 };
@@ -293,15 +306,15 @@ __device__ void residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, long 
             R.s[h][t] = e;
             l += e;
         }
-        R.m[h] = m;
-        R.l[h] = l;
+        sm.ro.m[h] = m;
+        sm.ro.l[h] = l;
     }
     __syncthreads();
     for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
         const int h = idx / kHeadDim, c = idx % kHeadDim;
         float o = 0.0f;
         for (int t = 0; t < nres; ++t) o = fmaf(R.s[h][t], R.v[t][c], o);
-        R.o[h][c] = o;
+        sm.ro.o[h][c] = o;
     }
     __syncthreads();
 }
@@ -381,8 +394,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     }
     const int full = L / kGroup, nres = L % kGroup;
     const int P = p.pages_per_split;
-    const int n_ps = (full + P - 1) / P;
-    if (split >= (n_ps > 0 ? n_ps : 1)) return;
+    const int n_ps = (full + P - 1) / P;               // splits with pages
+    const int n_work = n_ps > 0 ? n_ps : 1;             // workgroups of this (sequence, KV head)
+    if (split >= n_work) return;
+    // the residual tokens belong to the last split index (their loads overlap its first pages)
+    const bool has_res = nres > 0 && split == n_work - 1;
 
     const int wave = tid >> 6, lane = tid & 63;
     // ---- prologue: q, this wave's block-table ids and its first page are all requested
@@ -437,6 +453,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         }
     }
     __syncthreads();
+
+    if (has_res) residual_tokens<GS>(p, sm, bh, nres, G);
 
     const long long slot0 = bh * p.n_splits;
     if (n_ps > 0) {
@@ -660,59 +678,145 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 }
             }
         }
-        const bool bad = __syncthreads_or(bad_page);
+    }
+
+    // ---- this workgroup's merge: its waves' page states and, on the last split, the residual
+    const bool bad = __syncthreads_or(bad_page);
+    const bool single = n_work == 1;
+    {
+        const MergeLds<GS> &M = sm.u.merge;
         float *part_o = p.part_o + (slot0 + split) * G * kHeadDim;
         float *part_ml = p.part_ml + (slot0 + split) * G * 2;
         for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
             const int hh = idx / kHeadDim, c = idx % kHeadDim;
-            float m = -INFINITY;
+            float m = has_res ? sm.ro.m[hh] : -INFINITY;
+            if (n_ps > 0) {
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) m = fmaxf(m, M.m[w][hh]);
+                for (int w = 0; w < kWaves; ++w) m = fmaxf(m, M.m[w][hh]);
+            }
             float l = 0.0f, o = 0.0f;
+            if (has_res) {
+                const float wt = exp2f(sm.ro.m[hh] - m);
+                l = wt * sm.ro.l[hh];
+                o = wt * sm.ro.o[hh][c];
+            }
+            if (n_ps > 0) {
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float wt = M.m[w][hh] == -INFINITY ? 0.0f : exp2f(M.m[w][hh] - m);
-                l = fmaf(wt, M.l[w][hh], l);
-                o = fmaf(wt, M.o[w][hh][c], o);
+                for (int w = 0; w < kWaves; ++w) {
+                    const float wt = M.m[w][hh] == -INFINITY ? 0.0f : exp2f(M.m[w][hh] - m);
+                    l = fmaf(wt, M.l[w][hh], l);
+                    o = fmaf(wt, M.o[w][hh][c], o);
+                }
             }
-            store_dev(&part_o[idx], bad ? NAN : o);
-            if (c == 0) {
-                store_dev(&part_ml[2 * hh], bad ? 0.0f : m);
-                store_dev(&part_ml[2 * hh + 1], bad ? NAN : l);
+            if (single) {
+                out_bh[idx] = bad ? NAN : o / l;
+                if (lse_bh && c == 0) lse_bh[hh] = bad ? NAN : (m + log2f(l)) * kLn2;
+            } else {
+                store_dev(&part_o[idx], bad ? NAN : o);
+                if (c == 0) {
+                    store_dev(&part_ml[2 * hh], bad ? 0.0f : m);
+                    store_dev(&part_ml[2 * hh + 1], bad ? NAN : l);
+                }
             }
         }
-        wait_stores();
-        __syncthreads();
-        if (tid == 0)
-            sm.last = __hip_atomic_fetch_add(p.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_ps - 1;
-        __syncthreads();
-        if (!sm.last) return;
     }
+    if (single) return;
+    wait_stores();
+    __syncthreads();
+    if (tid == 0)
+        sm.last = __hip_atomic_fetch_add(p.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_work - 1;
+    __syncthreads();
+    if (!sm.last) return;
 
-    // ---- last split of this (sequence, KV head): residual tokens, then merge everything
-    if (nres > 0) residual_tokens<GS>(p, sm, bh, nres, G);
-    const ResidualLds<GS> &R = sm.u.res;
-    for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
-        const int g = idx / kHeadDim, c = idx % kHeadDim;
-        float m = nres > 0 ? R.m[g] : -INFINITY;
-        for (int s = 0; s < n_ps; ++s) m = fmaxf(m, load_dev(&p.part_ml[((slot0 + s) * G + g) * 2]));
-        float l = 0.0f, o = 0.0f;
-        if (nres > 0) {
-            const float w = exp2f(R.m[g] - m);
-            l = w * R.l[g];
-            o = w * R.o[g][c];
-        }
-        for (int s = 0; s < n_ps; ++s) {
-            const float ms = load_dev(&p.part_ml[((slot0 + s) * G + g) * 2]);
-            const float ls = load_dev(&p.part_ml[((slot0 + s) * G + g) * 2 + 1]);
-            const float w = exp2f(ms - m);
-            l = fmaf(w, ls, l);
-            o = fmaf(w, load_dev(&p.part_o[((slot0 + s) * G + g) * kHeadDim + c]), o);
-        }
-        out_bh[g * kHeadDim + c] = o / l;
-        if (lse_bh && c == 0) lse_bh[g] = (m + log2f(l)) * kLn2;
+    // ---- the last workgroup of this (sequence, KV head) to finish merges every split.
+    // (m, l) of a chunk of splits is staged in LDS; the o partials are read in batches of 8
+    // splits whose loads are all issued before any is used (device-scope loads go past the
+    // L2, so a dependent chain of them would cost one memory round trip per split).
+    constexpr int kItems = (HS * kHeadDim + kThreads - 1) / kThreads;
+    constexpr int kPer = kMergeChunk * 16 / kThreads;
+    constexpr int kBatch = 8;
+    CombineLds &C = sm.u.comb;
+    float mx[kItems], ls[kItems], os[kItems];
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        mx[it] = -INFINITY;
+        ls[it] = 0.0f;
+        os[it] = 0.0f;
     }
-    if (n_ps > 0 && tid == 0) __hip_atomic_store(p.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int c0 = 0; c0 < n_work; c0 += kMergeChunk) {
+        const int cnt = min(kMergeChunk, n_work - c0);
+        float mv[kPer], lv[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = tid + k * kThreads;
+            if (i < cnt * G) {
+                const float *src = p.part_ml + ((slot0 + c0 + i / G) * G + i % G) * 2;
+                mv[k] = load_dev(src);
+                lv[k] = load_dev(src + 1);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = tid + k * kThreads;
+            if (i < cnt * G) {
+                C.m[i / G][i % G] = mv[k];
+                C.l[i / G][i % G] = lv[k];
+            }
+        }
+        __syncthreads();
+        float mn[kItems];
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int idx = tid + it * kThreads;
+            const int g = idx / kHeadDim;
+            float mc = -INFINITY;
+            if (idx < G * kHeadDim)
+                for (int s2 = 0; s2 < cnt; ++s2) mc = fmaxf(mc, C.m[s2][g]);
+            mn[it] = fmaxf(mx[it], mc);
+            const float sc = mx[it] == -INFINITY ? 0.0f : exp2f(mx[it] - mn[it]);
+            ls[it] *= sc;
+            os[it] *= sc;
+            mx[it] = mn[it];
+        }
+        for (int s0 = 0; s0 < cnt; s0 += kBatch) {
+            float x[kItems][kBatch];
+#pragma unroll
+            for (int it = 0; it < kItems; ++it) {
+                const int idx = tid + it * kThreads;
+                const int g = idx / kHeadDim, c = idx % kHeadDim;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    x[it][k] = (idx < G * kHeadDim && s0 + k < cnt)
+                                   ? load_dev(p.part_o + ((slot0 + c0 + s0 + k) * G + g) * kHeadDim + c)
+                                   : 0.0f;
+            }
+#pragma unroll
+            for (int it = 0; it < kItems; ++it) {
+                const int idx = tid + it * kThreads;
+                const int g = idx / kHeadDim;
+                if (idx < G * kHeadDim) {
+#pragma unroll
+                    for (int k = 0; k < kBatch; ++k) {
+                        if (s0 + k < cnt) {
+                            const float w = exp2f(C.m[s0 + k][g] - mn[it]);
+                            ls[it] = fmaf(w, C.l[s0 + k][g], ls[it]);
+                            os[it] = fmaf(w, x[it][k], os[it]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const int idx = tid + it * kThreads;
+        if (idx < G * kHeadDim) {
+            out_bh[idx] = os[it] / ls[it];
+            if (lse_bh && idx % kHeadDim == 0) lse_bh[idx / kHeadDim] = (mx[it] + log2f(ls[it])) * kLn2;
+        }
+    }
+    if (tid == 0) __hip_atomic_store(p.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words)

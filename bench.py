@@ -43,7 +43,11 @@ CONFIGS = {
                  seed=20250205),
     "single": dict(workload="single layer K8V4, GQA 4, 512 tokens, fp32 K/V/q (attention only)",
                    pairs=[(8, 4)], n_q_heads=4, n_kv_heads=1, batch=1, context=512, n_outliers=4,
-                   seed=2024),
+                   seed=2024, f32=True),
+    "ragged": dict(workload="llama3.1-8b-shape C3.25 paged decode step, batch 256, lengths U{1024..32768}, "
+                            "shuffled page pool (append + attention, 32 layers)",
+                   pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=256, ragged=(1024, 32768), shuffle=True,
+                   n_outliers=3, seed=20250207),
     "pack": dict(workload="prefill pack, llama3.1-8b shape C3.25, 32768 tokens, batch 1 (32 layers)",
                  pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=1, context=32768, n_outliers=3,
                  seed=20250206),
@@ -77,13 +81,19 @@ def log(msg):
 
 
 def decode_alg_bytes(kb, vb, batch, H, Hq, L):
-    """Bytes one decode-attention launch must move: the pages covering the attended tokens
-    (codes + fp16 scale/zero), the live bf16 residual tokens (K and V), q (bf16), out (fp32)
-    and lse (fp32)."""
-    full, nres = L // 32, L % 32
-    pages = batch * H * full * 512 * (kb + vb + 2)
-    resid = batch * H * nres * 128 * 2 * 2
-    return pages + resid + batch * Hq * 128 * 2 + batch * Hq * 128 * 4 + batch * Hq * 4
+    """Bytes one decode-attention launch must move when every sequence attends over L
+    tokens: the pages covering the attended tokens (codes + fp16 scale/zero), the live bf16
+    residual tokens (K and V), q (bf16), out (fp32) and lse (fp32)."""
+    return ragged_decode_alg_bytes(kb, vb, [L] * batch, H, Hq)
+
+
+def ragged_decode_alg_bytes(kb, vb, lens, H, Hq):
+    """As decode_alg_bytes, for sequences attending over lens[b] tokens each."""
+    tot = 0
+    for L in lens:
+        full, nres = int(L) // 32, int(L) % 32
+        tot += H * full * 512 * (kb + vb + 2) + H * nres * 128 * 2 * 2
+    return tot + len(lens) * Hq * 128 * (2 + 4) + len(lens) * Hq * 4
 
 
 def append_alg_bytes(batch, H):
@@ -92,9 +102,17 @@ def append_alg_bytes(batch, H):
 
 
 class DecodeStack:
-    """Packed per-layer caches of a decode workload, resident on the device."""
+    """Packed per-layer caches of a decode workload, resident on the device.
+
+    Sequence b holds lens[b] tokens (C for every sequence, or seeded ragged lengths); its
+    logical pages 0 .. ceil((lens[b]+1)/32)-1 map to physical pages through one block table
+    shared by all layers (identity order, or a seeded permutation of the pool).  Sources are
+    generated on the device and packed in chunks of sequences, never materialized whole."""
+
+    CHUNK_BYTES = 2 << 30
 
     def __init__(self, cfg, device):
+        import numpy as np
         import torch
         import synth
         import layer_wise_mixed_kvq_amd as kvq
@@ -102,22 +120,48 @@ class DecodeStack:
         self.kvq = kvq
         pairs = cfg["pairs"]
         self.model = kvq.Model(pairs, cfg["n_q_heads"], cfg["n_kv_heads"])
-        B, H, C = cfg["batch"], cfg["n_kv_heads"], cfg["context"]
-        self.B, self.H, self.Hq, self.C = B, H, cfg["n_q_heads"], C
-        self.L = C + 1
-        self.max_pages = (self.L + 31) // 32
-        self.block_table = torch.arange(B * self.max_pages, dtype=torch.int32, device=device).view(B, self.max_pages)
-        self.caches, self.q, self.k_new, self.v_new, self.out, self.lse = [], [], [], [], [], []
+        B, H = cfg["batch"], cfg["n_kv_heads"]
         seed = cfg["seed"]
-        seq_len = torch.full((B,), C, dtype=torch.int32, device=device)
-        src_dtype = "f32" if cfg is CONFIGS["single"] else "bf16"
+        if "ragged" in cfg:
+            lens = synth.seq_lens(seed, B, *cfg["ragged"]).astype(np.int64)
+        else:
+            lens = np.full(B, cfg["context"], dtype=np.int64)
+        self.lens = lens
+        self.B, self.H, self.Hq, self.C = B, H, cfg["n_q_heads"], int(lens.max())
+        self.L = self.C + 1
+        n_log = (lens + 1 + 31) // 32                      # pages incl. room for the appended token
+        self.max_pages = int(n_log.max())
+        n_phys = int(n_log.sum())
+        perm = synth.permutation(seed, n_phys) if cfg.get("shuffle") else np.arange(n_phys, dtype=np.int32)
+        bt = np.zeros((B, self.max_pages), dtype=np.int32)
+        off = 0
+        for b in range(B):
+            bt[b, :n_log[b]] = perm[off:off + n_log[b]]
+            off += int(n_log[b])
+        self.block_table_host = bt
+        self.block_table = torch.from_numpy(bt).to(device)
+        self.caches, self.q, self.k_new, self.v_new, self.out, self.lse = [], [], [], [], [], []
+        src_dtype = "f32" if cfg.get("f32") else "bf16"
+        self.src_dtype = src_dtype
+        # sequences per pack chunk: bounded source bytes (K and V)
+        per_tok = H * 128 * (4 if src_dtype == "f32" else 2) * 2
+        order = np.arange(B)
         for l, _ in enumerate(pairs):
-            cache = kvq.LayerCache(self.model, l, B, self.max_pages, block_table=self.block_table, device=device)
+            cache = kvq.LayerCache(self.model, l, B, self.max_pages, n_pages=n_phys, block_table=self.block_table,
+                                   device=device)
             cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
-            k = synth.fill(seed, synth.KIND_K, l, B, C, H, chan_mult=cm, dtype=src_dtype, device=device)
-            v = synth.fill(seed, synth.KIND_V, l, B, C, H, dtype=src_dtype, device=device)
-            kvq.kvq_pack(self.model, l, cache, k, v, seq_len)
-            del k, v
+            b0 = 0
+            while b0 < B:
+                b1 = b0 + 1
+                while b1 < B and (b1 + 1 - b0) * int(lens[b0:b1 + 1].max()) * per_tok <= self.CHUNK_BYTES:
+                    b1 += 1
+                T = int(lens[b0:b1].max())
+                k = synth.fill(seed, synth.KIND_K, l, b1 - b0, T, H, b0=b0, chan_mult=cm, dtype=src_dtype, device=device)
+                v = synth.fill(seed, synth.KIND_V, l, b1 - b0, T, H, b0=b0, dtype=src_dtype, device=device)
+                sl = torch.from_numpy(lens[b0:b1].astype(np.int32)).to(device)
+                kvq.kvq_pack(self.model, l, cache.sub_batch(b0, b1), k, v, sl)
+                del k, v
+                b0 = b1
             self.caches.append(cache)
             self.k_new.append(synth.fill(seed, synth.KIND_K_NEW, l, B, 1, H, chan_mult=cm, device=device).view(B, H, 128))
             self.v_new.append(synth.fill(seed, synth.KIND_V_NEW, l, B, 1, H, device=device).view(B, H, 128))
@@ -126,8 +170,10 @@ class DecodeStack:
             self.out.append(torch.empty((B, self.Hq, 128), dtype=torch.float32, device=device))
             self.lse.append(torch.empty((B, self.Hq), dtype=torch.float32, device=device))
         torch.cuda.synchronize()
-        self.pos = torch.full((B,), C, dtype=torch.int32, device=device)
-        self.seq_len = torch.full((B,), self.L, dtype=torch.int32, device=device)
+        del order
+        self.pos = torch.from_numpy(lens.astype(np.int32)).to(device)
+        self.attend = lens + 1
+        self.seq_len = torch.from_numpy(self.attend.astype(np.int32)).to(device)
         self.workspace = kvq.new_workspace(self.model, B, self.L, 0, device)
 
     def decode_layer(self, l):
@@ -141,15 +187,13 @@ class DecodeStack:
             self.decode_layer(l)
 
     def alg_bytes(self, with_append=True):
-        tot = 0
-        for (kb, vb) in self.cfg["pairs"]:
-            tot += decode_alg_bytes(kb, vb, self.B, self.H, self.Hq, self.L)
-            if with_append:
-                tot += append_alg_bytes(self.B, self.H)
+        tot = sum(self.decode_bytes())
+        if with_append:
+            tot += len(self.cfg["pairs"]) * append_alg_bytes(self.B, self.H)
         return tot
 
     def decode_bytes(self):
-        return [decode_alg_bytes(kb, vb, self.B, self.H, self.Hq, self.L) for kb, vb in self.cfg["pairs"]]
+        return [ragged_decode_alg_bytes(kb, vb, self.attend, self.H, self.Hq) for kb, vb in self.cfg["pairs"]]
 
 
 def capture(fn):
@@ -201,33 +245,35 @@ def per_launch_durations(launch, n_items, reps):
 
 
 def cpu_baseline_decode(cfg, stack, n_seq):
-    """The CPU oracle, as it stands (single thread), on `n_seq` of the batch's sequences for
-    every layer: the same append + attention work of one decode step.  Packing the sample
-    (prefill) is not timed."""
+    """The CPU oracle, as it stands (single thread), on the batch's first `n_seq` sequences
+    for every layer: the same append + attention work of one decode step.  Packing the
+    sample (prefill) is not timed.  Returns (seconds, tokens attended in the sample)."""
     import numpy as np
+    import torch
     import oracle as orc
     import synth
-    seed, H, Hq, C = cfg["seed"], cfg["n_kv_heads"], cfg["n_q_heads"], cfg["context"]
-    maxp = (C + 1 + 31) // 32
-    bt = np.arange(maxp, dtype=np.int32).reshape(1, maxp)
-    t_total = 0.0
+    seed, H, Hq = cfg["seed"], cfg["n_kv_heads"], cfg["n_q_heads"]
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    t_total, attended = 0.0, 0
     for l, (kb, vb) in enumerate(cfg["pairs"]):
         cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
         for b in range(n_seq):
+            C = int(stack.lens[b])
+            maxp = (C + 1 + 31) // 32
+            bt = np.arange(maxp, dtype=np.int32).reshape(1, maxp)
             k = synth.fill(seed, synth.KIND_K, l, 1, C, H, b0=b, chan_mult=cm)
             v = synth.fill(seed, synth.KIND_V, l, 1, C, H, b0=b)
             kn = synth.fill(seed, synth.KIND_K_NEW, l, 1, 1, H, b0=b, chan_mult=cm).view(1, H, 128)
             vn = synth.fill(seed, synth.KIND_V_NEW, l, 1, 1, H, b0=b).view(1, H, 128)
             q = synth.fill(seed, synth.KIND_Q, l, 1, 1, Hq, b0=b).view(1, Hq, 128)
-            import torch
-            bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
             pages, rk, rv = orc.new_cache(kb, vb, H, 1, maxp)
             orc.pack(kb, vb, bits(k), bits(v), [C], bt, pages, rk, rv)
             t0 = time.perf_counter()
             orc.append(kb, vb, bits(kn), bits(vn), [C], bt, pages, rk, rv)
             orc.decode_attn(kb, vb, H, bits(q), [C + 1], bt, pages, rk, rv)
             t_total += time.perf_counter() - t0
-    return t_total
+            attended += C + 1
+    return t_total, attended
 
 
 def main():
@@ -305,10 +351,11 @@ def main():
     cpu = None
     if args.cpu_seqs > 0 and args.config != "single":
         log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequences x {n_layers} layers ...")
-        t_cpu = cpu_baseline_decode(cfg, stack, args.cpu_seqs)
+        t_cpu, attended = cpu_baseline_decode(cfg, stack, args.cpu_seqs)
         cpu = {"value": args.cpu_seqs / t_cpu, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{args.cpu_seqs} of {stack.B} sequences, all {n_layers} layers: append + binary64 "
-                         f"attention over {stack.L} tokens (packing of the sample not timed), single thread"}
+               "sample": f"{args.cpu_seqs} of {stack.B} sequences ({attended // n_layers} attended tokens per "
+                         f"layer), all {n_layers} layers: append + binary64 attention (packing of the sample "
+                         f"not timed), single thread"}
         log(f"[bench] CPU oracle {t_cpu:.1f} s -> {cpu['value']:.3f} tokens/s")
 
     rec = {
@@ -325,7 +372,7 @@ def main():
         "dtype": "bf16-in/fp32-acc, int2/4/8 codes",
         "data": "synthetic (seeded Irwin-Hall N(0,1) K/V/q, 3 outlier key channels x10 per layer and head)",
         "config": {"workload": cfg["workload"], "batch": stack.B, "context": stack.C,
-                   "attended_tokens": stack.L, "layers": n_layers, "n_q_heads": stack.Hq,
+                   "attended_tokens": stack.L, "mean_attended_tokens": float(stack.attend.mean()), "layers": n_layers, "n_q_heads": stack.Hq,
                    "n_kv_heads": stack.H, "head_dim": 128, "equiv_bits": kvq.kvq_equiv_bits(stack.model),
                    "graph": not args.no_graph},
         "packed_kv_gbps": step_bytes / (ms * 1e-3) / 1e9,

@@ -90,6 +90,17 @@ class LayerCache:
         assert block_table.is_contiguous()
         self.block_table = block_table
 
+    def sub_batch(self, b0: int, b1: int) -> "LayerCache":
+        """View of sequences b0 .. b1-1: the same page pool, their residual pages and
+        block-table rows.  Calls on the view touch only those sequences."""
+        assert 0 <= b0 < b1 <= self.batch
+        v = object.__new__(LayerCache)
+        v.layer, v.batch, v.max_pages, v.n_pages = self.layer, b1 - b0, self.max_pages, self.n_pages
+        v.pages = self.pages
+        v.resid_k, v.resid_v = self.resid_k[b0:b1], self.resid_v[b0:b1]
+        v.block_table = self.block_table[b0:b1]
+        return v
+
     def c_struct(self) -> KvqLayerCache:
         return KvqLayerCache(self.pages.data_ptr(), self.n_pages, self.resid_k.data_ptr(),
                              self.resid_v.data_ptr(), self.block_table.data_ptr(), self.batch,

@@ -79,11 +79,14 @@ __device__ __forceinline__ uint32_t split_lo(float x0, float y0, float x1, float
     return __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(r0), static_cast<_Float16>(r1)});
 }
 
-// LDS ordering inside one wave: every lane's earlier LDS stores are visible to the
-// wave's later LDS loads.
+// LDS ordering inside one wave: the LDS executes one wave's DS instructions in issue
+// order, so a read issued after a write of the same wave returns the written data without
+// waiting for the write to complete.  Only the compiler must keep the order: the barrier
+// stops it from moving LDS accesses across this point (the normal waits on read results
+// are still inserted where the data is used).
 __device__ __forceinline__ void wave_lds_sync()
 {
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_wave_barrier();
 }
 
@@ -93,7 +96,7 @@ __device__ __forceinline__ void wave_lds_sync()
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v)
 {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
 
@@ -157,25 +160,36 @@ __device__ __forceinline__ uint32_t fp16x2_1024()
     return m;
 }
 
-// Pair j (0..3) of operand `op` from a lane's packed codes, as exact normal fp16 integers:
-// with n = 16/BITS codes per 16-bit half, k = 4*op + j sits in word k / n at shift
-// BITS*(k % n) in both halves.  The code bits are inserted into 1024.0 (0x6400, spacing 1)
-// and one packed subtract removes the 1024.  The matrix cores keep full binary32 accuracy
-// only for normal fp16 inputs: subnormal operands lose about four bits in the accumulation.
+// Pair j (0..3) of operand `op` from a lane's packed codes, as exact normal fp16 values:
+// with n = 16/BITS codes per 16-bit half, k = 4*op + j sits in word k / n at position
+// p = k % n in both halves.  The m = 8/BITS positions of a half's low byte are inserted
+// in place into 1024.0 (0x6400: spacing 1, low ten bits zero); those of the high byte after
+// one shift by 8 (shared by every pair of the word).  After one packed subtract of 1024 the
+// pair is code * 2^unpack_shift<BITS>(j), exact; the power of two is divided out of the
+// matching A-operand element.  The matrix cores keep full binary32 accuracy only for normal
+// fp16 inputs: subnormal operands lose about four bits in the accumulation.
 // No inline asm writes a register here: the hazard recognizer does not see registers an
 // asm statement writes, and a register that is dead in an MFMA result can be reused while
 // that MFMA is still in flight, which has to wait until the MFMA retires.
 template <int BITS>
+__device__ __forceinline__ constexpr int unpack_shift(int j)
+{
+    return BITS * (j % (8 / BITS));
+}
+
+template <int BITS>
 __device__ __forceinline__ uint4 unpack_codes(const uint32_t *w, int op, uint32_t magic)
 {
-    constexpr int n = 16 / BITS;
+    constexpr int n = 16 / BITS, m = 8 / BITS;
     constexpr uint32_t M = ((1u << BITS) - 1u) * 0x00010001u;
     const half2_t bias = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-1024.0f)};
     uint32_t r[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int k = 4 * op + j;
-        const uint32_t y = ((w[k / n] >> (BITS * (k % n))) & M) | (magic & ~M);
+        const int k = 4 * op + j, p = k % n;
+        const uint32_t x = p >= m ? w[k / n] >> 8 : w[k / n];
+        const uint32_t Mp = M << (BITS * (p % m));
+        const uint32_t y = (x & Mp) | (magic & ~Mp);
         r[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, y) + bias);
     }
     return make_uint4(r[0], r[1], r[2], r[3]);
@@ -192,8 +206,10 @@ __device__ __forceinline__ int key_pair_channel(int jj, int j)
 
 template <int GS>
 struct WaveLds {
-    alignas(16) uint32_t qp[2][4 * GS + 1][64];      // (q s) hi / lo pairs: [part][head, + zero row][pair]
-    alignas(16) uint32_t pp[2][4][4 * GS + 1][16];   // (p s) hi / lo pairs: [part][value group][head][pair]
+    // rows padded by 4 words so that the 128-bit A-operand reads of different head rows
+    // fall into different LDS banks
+    alignas(16) uint32_t qp[2][4 * GS + 1][68];      // (q s) hi / lo pairs: [part][head, + zero row][pair]
+    alignas(16) uint32_t pp[2][4][4 * GS + 1][20];   // (p s) hi / lo pairs: [part][value group][head][pair]
     float p[32][4 * GS];                             // softmax weights of the page: [token][head]
     float alpha[4 * GS];
     float bv[4][4 * GS];                             // value zero terms at the end: [group][head]
@@ -268,16 +284,39 @@ __device__ __forceinline__ void wait_stores()
 // ------------------------------------------------------------------------------------
 // residual tokens (at most 31, bf16), plain VALU, into LDS: (m, l, o) per head
 // ------------------------------------------------------------------------------------
+// The residual rows are requested at kernel start (16-byte chunks i = tid, tid + 256 of
+// the 32 x 128 bf16 tile, rows below nres only) and attended after the pages, so their
+// load latency is hidden behind the page work.
+__device__ __forceinline__ void load_residual(const DecodeParams &p, long long bh, int nres, uint4 (&kv)[4])
+{
+    const uint4 *rk = reinterpret_cast<const uint4 *>(p.resid_k + bh * kGroup * kHeadDim);
+    const uint4 *rv = reinterpret_cast<const uint4 *>(p.resid_v + bh * kGroup * kHeadDim);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = threadIdx.x + k * kThreads;
+        const bool live = i / (kHeadDim / 8) < nres;
+        kv[k] = live ? rk[i] : make_uint4(0u, 0u, 0u, 0u);
+        kv[2 + k] = live ? rv[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 template <int GS>
-__device__ void residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, long long bh, int nres, int G)
+__device__ void residual_tokens(DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nres, int G)
 {
     ResidualLds<GS> &R = sm.u.res;
     const int tid = threadIdx.x;
-    const uint16_t *rk = p.resid_k + bh * kGroup * kHeadDim;
-    const uint16_t *rv = p.resid_v + bh * kGroup * kHeadDim;
-    for (int i = tid; i < nres * kHeadDim; i += kThreads) {
-        R.k[i / kHeadDim][i % kHeadDim] = bf16_bits_to_float(rk[i]);
-        R.v[i / kHeadDim][i % kHeadDim] = bf16_bits_to_float(rv[i]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = tid + k * kThreads, row = i / (kHeadDim / 8), col = 8 * (i % (kHeadDim / 8));
+        const uint32_t kw[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
+        const uint32_t vw[4] = {kv[2 + k].x, kv[2 + k].y, kv[2 + k].z, kv[2 + k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            R.k[row][col + 2 * e] = __uint_as_float(kw[e] << 16);
+            R.k[row][col + 2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+            R.v[row][col + 2 * e] = __uint_as_float(vw[e] << 16);
+            R.v[row][col + 2 * e + 1] = __uint_as_float(vw[e] & 0xFFFF0000u);
+        }
     }
     __syncthreads();
     // scores: thread (t, part) covers channels 16*part .. 16*part+15 of token t
@@ -375,7 +414,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     using PL = PageLayout<KB, VB>;
     constexpr int HS = 4 * GS;                 // head slots
     __shared__ DecodeSmem<GS> sm;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // grid (H, batch, splits): the split index varies slowest, so every (sequence, KV head)
+    // has its split 0 dispatched first
+    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x;
     const int G = p.G;
     const long long bh = static_cast<long long>(b) * p.H + h;
@@ -397,8 +438,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const int n_ps = (full + P - 1) / P;               // splits with pages
     const int n_work = n_ps > 0 ? n_ps : 1;             // workgroups of this (sequence, KV head)
     if (split >= n_work) return;
-    // the residual tokens belong to the last split index (their loads overlap its first pages)
-    const bool has_res = nres > 0 && split == n_work - 1;
+    // the residual tokens belong to split 0: the first workgroups dispatched absorb the extra
+    // work while the last ones are still starting
+    const bool has_res = nres > 0 && split == 0;
 
     const int wave = tid >> 6, lane = tid & 63;
     // ---- prologue: q, this wave's block-table ids and its first page are all requested
@@ -415,26 +457,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
     int my_phys = 0;
     if (lane < n_my) my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + pg_begin + kWaves * lane];
+    uint4 res_kv[4];
+    if (has_res) load_residual(p, bh, nres, res_kv);
     // lane roles in the page loop
     const int a = lane >> 4, r16 = lane & 15;
     const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
     const int ch0 = 32 * kq + key_pair_channel<KB>(kjj, kj);
     const int ch1 = ch0 + 16 / KB;
     const int t0 = 8 * (r16 >> 2) + (r16 & 3), t1 = t0 + 4;   // value pair this lane folds (group a)
+    // powers of two the code unpack leaves on this lane's key channels / value tokens
+    const int kshift = unpack_shift<KB>(kj), vshift = unpack_shift<VB>(r16 & 3);
     const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
-    auto page_base = [&](int j, bool &ok) -> const uint8_t * {
+    // page ids outside the pool mark the sequence bad (NaN outputs) and are read as page 0
+    const bool id_bad = lane < n_my && (my_phys < 0 || my_phys >= p.n_pages);
+    const bool bad_page = __any(id_bad);
+    if (id_bad) my_phys = 0;
+    auto page_base = [&](int j) -> const uint8_t * {
         const int phys = __builtin_amdgcn_readlane(my_phys, j);
-        ok = phys >= 0 && phys < p.n_pages;
-        return pool + (static_cast<long long>(ok ? phys : 0) * p.H + h) * PL::kBytes;
+        return pool + (static_cast<long long>(phys) * p.H + h) * PL::kBytes;
     };
-    bool bad_page = false;
     PageRegs<KB, VB> cur, nxt;
-    if (n_my > 0) {
-        bool ok;
-        const uint8_t *base = page_base(0, ok);
-        bad_page |= !ok;
-        load_page<KB, VB>(cur, base, lane, ch0, ch1, t0, t1);
-    }
+    if (n_my > 0) load_page<KB, VB>(cur, page_base(0), lane, ch0, ch1, t0, t1);
 #pragma unroll
     for (int k = 0; k < kQPer; ++k) {
         const int i = tid + k * kThreads;
@@ -453,8 +496,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         }
     }
     __syncthreads();
-
-    if (has_res) residual_tokens<GS>(p, sm, bh, nres, G);
 
     const long long slot0 = bh * p.n_splits;
     if (n_ps > 0) {
@@ -515,8 +556,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             }
             // ---- fold key scales into q: two channels x every head slot, hi/lo ---------
             {
-                const float s0 = ldexpf(half_bits_to_float(cur.kszw[0] & 0xFFFFu), E);
-                const float s1 = ldexpf(half_bits_to_float(cur.kszw[1] & 0xFFFFu), E);
+                const float s0 = ldexpf(half_bits_to_float(cur.kszw[0] & 0xFFFFu), E - kshift);
+                const float s1 = ldexpf(half_bits_to_float(cur.kszw[1] & 0xFFFFu), E - kshift);
 #pragma unroll
                 for (int hh = 0; hh < HS; ++hh) {
                     const uint32_t hi = split_hi(qw[hh][0] * s0, qw[hh][1] * s1);
@@ -606,8 +647,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             wave_lds_sync();
             // ---- fold value scales into p: two tokens x every head slot, hi/lo ----------
             {
-                const float sv0 = ldexpf(half_bits_to_float(cur.vszw[0] & 0xFFFFu), ev);
-                const float sv1 = ldexpf(half_bits_to_float(cur.vszw[1] & 0xFFFFu), ev);
+                const float sv0 = ldexpf(half_bits_to_float(cur.vszw[0] & 0xFFFFu), ev - vshift);
+                const float sv1 = ldexpf(half_bits_to_float(cur.vszw[1] & 0xFFFFu), ev - vshift);
                 const float zv0 = half_bits_to_float(cur.vszw[0] >> 16);
                 const float zv1 = half_bits_to_float(cur.vszw[1] >> 16);
 #pragma unroll
@@ -633,20 +674,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 }
             }
         };
-        // two page buffers in turn: page j+1 is in flight while page j is processed
+        // two page buffers in fixed roles: page j+1 is in flight while page j is processed.
+        // Every prefetch is unconditional (past the wave's last page it reloads that page,
+        // an L2 hit), so the compiler's wait counts see one path and wait only for the page
+        // about to be used, never for the one just requested.
         auto prefetch = [&](PageRegs<KB, VB> &dst, int j) {
-            bool ok;
-            const uint8_t *base = page_base(j, ok);
-            bad_page |= !ok;
-            load_page<KB, VB>(dst, base, lane, ch0, ch1, t0, t1);
+            load_page<KB, VB>(dst, page_base(min(j, n_my - 1)), lane, ch0, ch1, t0, t1);
         };
-        for (int j = 0; j < n_my; j += 2) {
-            if (j + 1 < n_my) prefetch(nxt, j + 1);
+        int j = 0;
+        for (; j + 1 < n_my; j += 2) {
+            prefetch(nxt, j + 1);
             process_page(cur);
-            if (j + 1 >= n_my) break;
-            if (j + 2 < n_my) prefetch(cur, j + 2);
+            prefetch(cur, j + 2);
             process_page(nxt);
         }
+        if (j < n_my) process_page(cur);
 
         // ---- this wave's state: l per head, value zero terms, unnormalized output -------
         float lw[GS];
@@ -664,7 +706,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(acc[nb][i], unscale, W.bv[nb >> 1][4 * i + a]);
-        __syncthreads();     // every wave is done with its WaveLds: reuse the space to merge
+        __syncthreads();     // every wave is done with its WaveLds: reuse the space
+        if (has_res) residual_tokens<GS>(sm, res_kv, nres, G);
         MergeLds<GS> &M = sm.u.merge;
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
@@ -678,6 +721,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 }
             }
         }
+    } else if (has_res) {
+        residual_tokens<GS>(sm, res_kv, nres, G);
     }
 
     // ---- this workgroup's merge: its waves' page states and, on the last split, the residual
@@ -745,6 +790,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     }
     for (int c0 = 0; c0 < n_work; c0 += kMergeChunk) {
         const int cnt = min(kMergeChunk, n_work - c0);
+        float x[kItems][kBatch];
+        auto load_o = [&](int s0) {
+#pragma unroll
+            for (int it = 0; it < kItems; ++it) {
+                const int idx = tid + it * kThreads;
+                const int g = idx / kHeadDim, c = idx % kHeadDim;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    x[it][k] = (idx < G * kHeadDim && s0 + k < cnt)
+                                   ? load_dev(p.part_o + ((slot0 + c0 + s0 + k) * G + g) * kHeadDim + c)
+                                   : 0.0f;
+            }
+        };
         float mv[kPer], lv[kPer];
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
@@ -755,6 +813,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 lv[k] = load_dev(src + 1);
             }
         }
+        load_o(0);      // in flight together with the (m, l) loads
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int i = tid + k * kThreads;
@@ -779,17 +838,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             mx[it] = mn[it];
         }
         for (int s0 = 0; s0 < cnt; s0 += kBatch) {
-            float x[kItems][kBatch];
-#pragma unroll
-            for (int it = 0; it < kItems; ++it) {
-                const int idx = tid + it * kThreads;
-                const int g = idx / kHeadDim, c = idx % kHeadDim;
-#pragma unroll
-                for (int k = 0; k < kBatch; ++k)
-                    x[it][k] = (idx < G * kHeadDim && s0 + k < cnt)
-                                   ? load_dev(p.part_o + ((slot0 + c0 + s0 + k) * G + g) * kHeadDim + c)
-                                   : 0.0f;
-            }
+            if (s0 > 0) load_o(s0);
 #pragma unroll
             for (int it = 0; it < kItems; ++it) {
                 const int idx = tid + it * kThreads;
@@ -829,7 +878,7 @@ __global__ void zero_fill_kernel(uint32_t *p, size_t n_words)
 template <int KB, int VB, int GS>
 hipError_t launch_decode_g(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
-    dim3 grid(p.n_splits, p.H, p.batch);
+    dim3 grid(p.H, p.batch, p.n_splits);
     if (q_f32)
         hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float>), grid, dim3(kThreads), 0, s, p);
     else

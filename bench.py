@@ -52,7 +52,16 @@ CONFIGS = {
                  pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=1, context=32768, n_outliers=3,
                  seed=20250206),
     "copy": dict(workload="streaming copy: 1 GiB int32 read + 1 GiB written (torch bitwise_not)"),
+    "sweep": dict(workload="uniform-pair sweep, llama3.1-8b shape, 32 layers: decode step tokens/s per table "
+                           "relative to KV8 at the (batch, input length) points of the pages' throughput table "
+                           "and at (16, 4096)"),
 }
+
+# per-layer tables of the sweep: uniform pairs of the pages' throughput comparison and the
+# mixed 3.25-bit table
+SWEEP_TABLES = {"KV8": [(8, 8)] * 32, "K8V4": [(8, 4)] * 32, "KV4": [(4, 4)] * 32, "K4V2": [(4, 2)] * 32,
+                "C3.25": LLAMA_C325}
+SWEEP_SHAPES = [(64, 128), (16, 512), (8, 1024), (16, 4096)]
 
 
 # sources the decode kernel is built from: a stored HBM-traffic measurement is reported only
@@ -304,6 +313,8 @@ def main():
         return bench_pack(cfg, args)
     if args.config == "copy":
         return bench_copy(args)
+    if args.config == "sweep":
+        return bench_sweep(args)
 
     log(f"[bench] building {args.config} cache ...")
     t0 = time.perf_counter()
@@ -435,6 +446,44 @@ def bench_pack(cfg, args):
                      "avg_launch_us": launch_us, "alg_bytes_per_launch": (src_bytes + page_bytes) / len(caches)},
         "cpu_baseline": None,
     }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_sweep(args):
+    """Decode step (append + attention, 32 layers, Llama-3.1-8B heads) for each table of
+    SWEEP_TABLES at each (batch, cached tokens) of SWEEP_SHAPES; tokens/s and the ratio to
+    the uniform 8-bit table, the shape of the pages' throughput comparison at kernel level."""
+    import torch
+    dev = torch.device("cuda:0")
+    rows = []
+    for batch, ctx in SWEEP_SHAPES:
+        row = {"batch": batch, "input_len": ctx, "tokens_per_s": {}, "ms_per_step": {}, "decode_gbps": {}}
+        for name, pairs in SWEEP_TABLES.items():
+            cfg = dict(CONFIGS["llama"], pairs=pairs, batch=batch, context=ctx)
+            stack = DecodeStack(cfg, dev)
+            g = capture(lambda: stack.step(True))
+            ms, _ = time_graph(g, args.steps, args.warmup)
+            g_attn = capture(lambda: stack.step(False))
+            ms_attn, _ = time_graph(g_attn, args.steps, 2)
+            row["tokens_per_s"][name] = batch * 1000.0 / ms
+            row["ms_per_step"][name] = ms
+            row["decode_gbps"][name] = sum(stack.decode_bytes()) / (ms_attn * 1e-3) / 1e9
+            log(f"[bench] sweep B={batch} L={ctx} {name}: {ms:.4f} ms/step, {row['tokens_per_s'][name]:.0f} tok/s, "
+                f"decode {row['decode_gbps'][name]:.0f} GB/s")
+            del g, g_attn, stack
+            torch.cuda.empty_cache()
+        base = row["tokens_per_s"]["KV8"]
+        row["relative_to_KV8"] = {k: v / base for k, v in row["tokens_per_s"].items()}
+        rows.append(row)
+    head = rows[-1]
+    rec = {"metric": "decode step tokens/s of the C3.25 table relative to uniform KV8 (llama3.1-8b shape, B=16, "
+                     "4096 cached tokens), 1 GPU",
+           "value": head["relative_to_KV8"]["C3.25"], "unit": "x (ratio)", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["ms_per_step"]["C3.25"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16-in/fp32-acc, int2/4/8 codes", "data": "synthetic",
+           "config": {"workload": CONFIGS["sweep"]["workload"], "tables": list(SWEEP_TABLES),
+                      "shapes": SWEEP_SHAPES},
+           "sweep": rows, "roofline": None, "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
 

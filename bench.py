@@ -189,8 +189,15 @@ class DecodeStack:
         self.kvq.kvq_decode_attn(self.model, l, self.caches[l], self.q[l], self.seq_len, self.L,
                                  out=self.out[l], lse=self.lse[l], workspace=self.workspace)
 
-    def step(self, with_append=True):
+    def step(self, with_append=True, fused=True):
+        """One decode step over every layer: the new token's append (fused into the attention
+        launch, or as its own kvq_append launch) and attention over C + 1 tokens."""
         for l in range(len(self.caches)):
+            if with_append and fused:
+                self.kvq.kvq_append_decode_attn(self.model, l, self.caches[l], self.k_new[l], self.v_new[l],
+                                                self.pos, self.q[l], self.L, out=self.out[l], lse=self.lse[l],
+                                                workspace=self.workspace)
+                continue
             if with_append:
                 self.kvq.kvq_append(self.model, l, self.caches[l], self.k_new[l], self.v_new[l], self.pos)
             self.decode_layer(l)
@@ -294,6 +301,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-baseline sample (0 = skip)")
     ap.add_argument("--roofline-reps", type=int, default=5)
+    ap.add_argument("--unfused", action="store_true", help="append as its own launch before each attention launch")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -322,7 +330,7 @@ def main():
     log(f"[bench] cache built in {time.perf_counter() - t0:.1f} s")
 
     with_append = args.config != "single"
-    step_fn = (lambda: stack.step(with_append))
+    step_fn = (lambda: stack.step(with_append, fused=not args.unfused))
     if args.no_graph:
         for _ in range(args.warmup):
             step_fn()
@@ -339,10 +347,15 @@ def main():
         g = capture(step_fn)
         log("[bench] graph captured; timing")
         ms, wall = time_graph(g, args.steps, args.warmup)
-    # attention-only step
+    # attention-only step, and the step with the append as its own launch (context)
     g_attn = capture(lambda: stack.step(False))
     ms_attn, _ = time_graph(g_attn, args.steps, 2)
-    log(f"[bench] step {ms:.4f} ms (attention only {ms_attn:.4f} ms)")
+    ms_unfused = None
+    if with_append and not args.unfused:
+        g_unf = capture(lambda: stack.step(True, fused=False))
+        ms_unfused, _ = time_graph(g_unf, args.steps, 2)
+        del g_unf
+    log(f"[bench] step {ms:.4f} ms (attention only {ms_attn:.4f} ms, append as its own launch {ms_unfused} ms)")
 
     # the dominant kernel (decode attention): its average launch duration is the
     # attention-only step (one launch per layer, replayed as a graph on the stream the kernels
@@ -385,11 +398,12 @@ def main():
         "config": {"workload": cfg["workload"], "batch": stack.B, "context": stack.C,
                    "attended_tokens": stack.L, "mean_attended_tokens": float(stack.attend.mean()), "layers": n_layers, "n_q_heads": stack.Hq,
                    "n_kv_heads": stack.H, "head_dim": 128, "equiv_bits": kvq.kvq_equiv_bits(stack.model),
-                   "graph": not args.no_graph},
+                   "graph": not args.no_graph, "fused_append": with_append and not args.unfused},
         "packed_kv_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "packed_kv_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "step_alg_bytes": step_bytes,
         "attention_only_ms_per_step": ms_attn,
+        "unfused_append_ms_per_step": ms_unfused,
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),

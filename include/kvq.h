@@ -181,6 +181,26 @@ kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_laye
                            int32_t max_seq_len, int32_t pages_per_split, float *out, float *lse,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* kvq_append followed by kvq_decode_attn over pos[b] + 1 tokens, in one launch.
+ * Only the new token is quantized online, inside the attention step.
+ *   [KVTuner OpenReview discussion, reply to reviewer 3, section 1 "Computational cost"]
+ *   [KVTuner OpenReview discussion, reply to reviewer 2, section 1, "Throughput
+ *    definition" (quantization overhead counts in throughput)]
+ * Arguments as for kvq_append (k_new, v_new, pos) and kvq_decode_attn (the rest); there is
+ * no seq_len: sequence b attends over pos[b] + 1 tokens, which must not exceed max_seq_len.
+ * Afterwards the cache holds exactly what kvq_append leaves (same bytes): the token in
+ * residual slot pos mod 32 and, when that slot is 31, the 32 residual tokens quantized into
+ * page pos / 32 (its block-table entry must be set).  That page is attended as quantized.
+ * The outputs equal kvq_decode_attn's after kvq_append up to floating-point rounding.  The
+ * workspace is the one kvq_decode_workspace_bytes sizes for (batch, max_seq_len).  pos is
+ * not advanced, so a repeated call with the same pos is idempotent.  pos[b] < 0 or
+ * pos[b] + 1 > max_seq_len yields NaN outputs for that sequence. */
+kvq_status kvq_append_decode_attn(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                                  const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,
+                                  kvq_dtype q_dtype, const void *q, int32_t max_seq_len,
+                                  int32_t pages_per_split, float *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

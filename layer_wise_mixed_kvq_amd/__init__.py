@@ -22,7 +22,7 @@ from ._native import KVQ_BF16, KVQ_F32, KvqError, KvqLayerCache, KvqModel, check
 HEAD_DIM = 128
 GROUP = 32
 
-__all__ = ["Model", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn",
+__all__ = ["Model", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_head_page_bytes",
            "kvq_page_bytes", "kvq_equiv_bits", "kvq_format_version", "lib"]
 
@@ -205,4 +205,36 @@ def kvq_decode_attn(model: Model, layer: int, cache: LayerCache, q, seq_len, max
                                 out.data_ptr(), lse.data_ptr() if lse is not False else None,
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 _stream(stream)), "kvq_decode_attn")
+    return out, lse
+
+
+def kvq_append_decode_attn(model: Model, layer: int, cache: LayerCache, k_new, v_new, pos, q, max_seq_len: int,
+                           pages_per_split: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """kvq_append of one bf16 token per sequence followed by decode attention over pos + 1
+    tokens, in one launch.  Returns (out, lse) as kvq_decode_attn."""
+    import torch
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (pos, "pos"), (q, "q")):
+        _dev(t, n)
+    shape = (cache.batch, model.n_kv_heads, HEAD_DIM)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new / v_new must be {shape}")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("k_new / v_new must be bfloat16")
+    if pos.dtype != torch.int32 or pos.numel() != cache.batch:
+        raise ValueError("pos must be int32 [batch]")
+    if tuple(q.shape) != (cache.batch, model.n_q_heads, HEAD_DIM):
+        raise ValueError(f"q must be [{cache.batch}][{model.n_q_heads}][128]")
+    if out is None:
+        out = torch.empty((cache.batch, model.n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((cache.batch, model.n_q_heads), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(model, cache.batch, max_seq_len, pages_per_split, q.device)
+    cs = cache.c_struct()
+    check(lib().kvq_append_decode_attn(ctypes.byref(model.c), layer, ctypes.byref(cs), k_new.data_ptr(),
+                                       v_new.data_ptr(), pos.data_ptr(), _dtype_code(q), q.data_ptr(),
+                                       max_seq_len, pages_per_split, out.data_ptr(),
+                                       lse.data_ptr() if lse is not False else None, workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+          "kvq_append_decode_attn")
     return out, lse

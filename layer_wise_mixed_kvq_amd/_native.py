@@ -14,7 +14,7 @@ KVQ_BF16, KVQ_F32 = 0, 1
 
 EXPORTED = ("kvq_status_str", "kvq_format_version", "kvq_head_page_bytes", "kvq_page_bytes",
             "kvq_equiv_bits", "kvq_validate_model", "kvq_pack", "kvq_append",
-            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_decode_attn")
+            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_decode_attn", "kvq_append_decode_attn")
 
 
 class KvqModel(ctypes.Structure):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_workspace_init.restype = ctypes.c_int
         L.kvq_decode_attn.argtypes = [mp, i32, cp, ctypes.c_int, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.kvq_decode_attn.restype = ctypes.c_int
+        L.kvq_append_decode_attn.argtypes = [mp, i32, cp, vp, vp, vp, ctypes.c_int, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.kvq_append_decode_attn.restype = ctypes.c_int
         _lib = L
     return _lib
 

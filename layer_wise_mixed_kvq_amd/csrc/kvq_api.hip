@@ -168,14 +168,16 @@ kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, void *str
     return hip_status(kvq::launch_zero_fill(workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
-kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
-                           kvq_dtype q_dtype, const void *q, const int32_t *seq_len, int32_t max_seq_len,
-                           int32_t pages_per_split, float *out, float *lse, void *workspace,
-                           size_t workspace_bytes, void *stream)
+namespace {
+
+kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache, kvq_dtype q_dtype,
+                         const void *q, const int32_t *seq_len, const uint16_t *k_new, const uint16_t *v_new,
+                         const int32_t *pos, int32_t max_seq_len, int32_t pages_per_split, float *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream)
 {
     kvq_status s = check_layer(model, layer, cache);
     if (s != KVQ_OK) return s;
-    if (!q || !seq_len || !out || max_seq_len < 0 || pages_per_split < 0) return KVQ_ERR_INVALID_ARG;
+    if (!q || !out || max_seq_len < 0 || pages_per_split < 0) return KVQ_ERR_INVALID_ARG;
     if (q_dtype != KVQ_BF16 && q_dtype != KVQ_F32) return KVQ_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return KVQ_ERR_ALIGNMENT;
@@ -190,6 +192,9 @@ kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_laye
     char *w = static_cast<char *>(workspace);
     p.q = q;
     p.seq_len = seq_len;
+    p.pos = pos;
+    p.k_new = k_new;
+    p.v_new = v_new;
     p.block_table = cache->block_table;
     p.pages = cache->pages;
     p.resid_k = cache->resid_k;
@@ -209,6 +214,29 @@ kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_laye
     p.n_splits = n_splits;
     return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], p,
                                          q_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+kvq_status kvq_decode_attn(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                           kvq_dtype q_dtype, const void *q, const int32_t *seq_len, int32_t max_seq_len,
+                           int32_t pages_per_split, float *out, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    if (!seq_len) return KVQ_ERR_INVALID_ARG;
+    return decode_common(model, layer, cache, q_dtype, q, seq_len, nullptr, nullptr, nullptr, max_seq_len,
+                         pages_per_split, out, lse, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_append_decode_attn(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                                  const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,
+                                  kvq_dtype q_dtype, const void *q, int32_t max_seq_len, int32_t pages_per_split,
+                                  float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!k_new || !v_new || !pos) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
+    return decode_common(model, layer, cache, q_dtype, q, nullptr, k_new, v_new, pos, max_seq_len,
+                         pages_per_split, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

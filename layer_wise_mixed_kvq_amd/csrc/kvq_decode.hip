@@ -39,6 +39,7 @@
 // h / 4 of the accumulator: with G <= 4 every lane holds exactly one head per token.
 //   scores:  D[head][token]   = A(q s hi|lo, from LDS)    x B(key codes, token-major rows)
 //   values:  D[head][channel] = A(p s hi|lo, from LDS)    x B(value codes, chunk layout)
+#include "kvq_codec.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -223,9 +224,8 @@ struct MergeLds {
 };
 
 template <int GS>
-struct ResidualLds {              // staging of the residual tokens
-    float k[kGroup][kHeadDim];
-    float v[kGroup][kHeadDim];
+struct ResidualLds {              // staging of the residual tokens (page-codec layout)
+    QuantSmem q;
     float s[4 * GS][kGroup];
 };
 
@@ -287,21 +287,31 @@ __device__ __forceinline__ void wait_stores()
 // The residual rows are requested at kernel start (16-byte chunks i = tid, tid + 256 of
 // the 32 x 128 bf16 tile, rows below nres only) and attended after the pages, so their
 // load latency is hidden behind the page work.
-__device__ __forceinline__ void load_residual(const DecodeParams &p, long long bh, int nres, uint4 (&kv)[4])
+// With the fused append the last row (nres - 1) is the new token, read from k_new / v_new.
+__device__ __forceinline__ void load_residual(const DecodeParams &p, long long bh, int nres, bool append,
+                                              uint4 (&kv)[4])
 {
     const uint4 *rk = reinterpret_cast<const uint4 *>(p.resid_k + bh * kGroup * kHeadDim);
     const uint4 *rv = reinterpret_cast<const uint4 *>(p.resid_v + bh * kGroup * kHeadDim);
+    const uint4 *nk = reinterpret_cast<const uint4 *>(p.k_new + bh * kHeadDim);
+    const uint4 *nv = reinterpret_cast<const uint4 *>(p.v_new + bh * kHeadDim);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const int i = threadIdx.x + k * kThreads;
-        const bool live = i / (kHeadDim / 8) < nres;
-        kv[k] = live ? rk[i] : make_uint4(0u, 0u, 0u, 0u);
-        kv[2 + k] = live ? rv[i] : make_uint4(0u, 0u, 0u, 0u);
+        const int i = threadIdx.x + k * kThreads, row = i / (kHeadDim / 8), col = i % (kHeadDim / 8);
+        const bool live = row < nres;
+        const bool fresh = append && row == nres - 1;
+        kv[k] = !live ? make_uint4(0u, 0u, 0u, 0u) : fresh ? nk[col] : rk[i];
+        kv[2 + k] = !live ? make_uint4(0u, 0u, 0u, 0u) : fresh ? nv[col] : rv[i];
     }
 }
 
-template <int GS>
-__device__ void residual_tokens(DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nres, int G)
+// Fused append: the new token (row nres - 1) is also stored into its residual slot; when it
+// completes a group (flush) the 32 rows are quantized into their page `flush_page` (same
+// codec and bytes as kvq_append) and the tile is replaced by its dequantized values, which
+// are then attended.  Returns false if the flush page id is outside the pool.
+template <int KB, int VB, int GS>
+__device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nres, int G,
+                                long long bh, bool append, bool flush, int flush_page)
 {
     ResidualLds<GS> &R = sm.u.res;
     const int tid = threadIdx.x;
@@ -312,13 +322,29 @@ __device__ void residual_tokens(DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nr
         const uint32_t vw[4] = {kv[2 + k].x, kv[2 + k].y, kv[2 + k].z, kv[2 + k].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            R.k[row][col + 2 * e] = __uint_as_float(kw[e] << 16);
-            R.k[row][col + 2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
-            R.v[row][col + 2 * e] = __uint_as_float(vw[e] << 16);
-            R.v[row][col + 2 * e + 1] = __uint_as_float(vw[e] & 0xFFFF0000u);
+            R.q.k[row * kTileStride + col + 2 * e] = __uint_as_float(kw[e] << 16);
+            R.q.k[row * kTileStride + col + 2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+            R.q.v[row * kTileStride + col + 2 * e] = __uint_as_float(vw[e] << 16);
+            R.q.v[row * kTileStride + col + 2 * e + 1] = __uint_as_float(vw[e] & 0xFFFF0000u);
+        }
+        if (append && row == nres - 1) {
+            reinterpret_cast<uint4 *>(p.resid_k + bh * kGroup * kHeadDim)[i] = kv[k];
+            reinterpret_cast<uint4 *>(p.resid_v + bh * kGroup * kHeadDim)[i] = kv[2 + k];
         }
     }
     __syncthreads();
+    bool ok = true;
+    if (flush) {
+        const int b = static_cast<int>(bh / p.H), h = static_cast<int>(bh % p.H);
+        const int phys = p.block_table[static_cast<long long>(b) * p.max_pages + flush_page];
+        ok = phys >= 0 && phys < p.n_pages;
+        if (ok) {
+            uint8_t *dst = static_cast<uint8_t *>(p.pages) +
+                           (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
+            quantize_page<KB, VB, true>(R.q, dst);
+        }
+        __syncthreads();
+    }
     // scores: thread (t, part) covers channels 16*part .. 16*part+15 of token t
     {
         const int t = tid >> 3, part = tid & 7;
@@ -326,7 +352,7 @@ __device__ void residual_tokens(DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nr
             float s = 0.0f;
             if (t < nres) {
 #pragma unroll
-                for (int x = 0; x < 16; ++x) s = fmaf(sm.qs[h][16 * part + x], R.k[t][16 * part + x], s);
+                for (int x = 0; x < 16; ++x) s = fmaf(sm.qs[h][16 * part + x], R.q.k[t * kTileStride + 16 * part + x], s);
             }
             s += __shfl_xor(s, 1);
             s += __shfl_xor(s, 2);
@@ -352,10 +378,11 @@ __device__ void residual_tokens(DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nr
     for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
         const int h = idx / kHeadDim, c = idx % kHeadDim;
         float o = 0.0f;
-        for (int t = 0; t < nres; ++t) o = fmaf(R.s[h][t], R.v[t][c], o);
+        for (int t = 0; t < nres; ++t) o = fmaf(R.s[h][t], R.q.v[t * kTileStride + c], o);
         sm.ro.o[h][c] = o;
     }
     __syncthreads();
+    return ok;
 }
 
 // ------------------------------------------------------------------------------------
@@ -422,9 +449,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const long long bh = static_cast<long long>(b) * p.H + h;
     float *out_bh = p.out + bh * G * kHeadDim;
     float *lse_bh = p.lse ? p.lse + bh * G : nullptr;
-    const int L = p.seq_len[b];
+    const bool append = p.pos != nullptr;      // fused append: attend over pos + 1 tokens
+    const int L = append ? p.pos[b] + 1 : p.seq_len[b];
 
-    const bool bad_len = L < 0 || L > p.max_seq_len || L > kGroup * p.max_pages;
+    const bool bad_len = (append ? L <= 0 : L < 0) || L > p.max_seq_len || L > kGroup * p.max_pages;
     if (bad_len || L == 0) {
         if (split == 0) {
             const float o = bad_len ? NAN : 0.0f;
@@ -433,7 +461,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         }
         return;
     }
-    const int full = L / kGroup, nres = L % kGroup;
+    // a fused append that completes a group quantizes that page itself (split 0) and attends
+    // over it from LDS: the pool supplies only the pages that existed before this call
+    const bool flush = append && L % kGroup == 0;
+    const int full = L / kGroup - (flush ? 1 : 0);      // pages read from the pool
+    const int nres = flush ? kGroup : L % kGroup;       // tokens attended from the residual tile
     const int P = p.pages_per_split;
     const int n_ps = (full + P - 1) / P;               // splits with pages
     const int n_work = n_ps > 0 ? n_ps : 1;             // workgroups of this (sequence, KV head)
@@ -458,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     int my_phys = 0;
     if (lane < n_my) my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + pg_begin + kWaves * lane];
     uint4 res_kv[4];
-    if (has_res) load_residual(p, bh, nres, res_kv);
+    if (has_res) load_residual(p, bh, nres, append, res_kv);
     // lane roles in the page loop
     const int a = lane >> 4, r16 = lane & 15;
     const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
@@ -470,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
     // page ids outside the pool mark the sequence bad (NaN outputs) and are read as page 0
     const bool id_bad = lane < n_my && (my_phys < 0 || my_phys >= p.n_pages);
-    const bool bad_page = __any(id_bad);
+    bool bad_page = __any(id_bad);
     if (id_bad) my_phys = 0;
     auto page_base = [&](int j) -> const uint8_t * {
         const int phys = __builtin_amdgcn_readlane(my_phys, j);
@@ -707,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(acc[nb][i], unscale, W.bv[nb >> 1][4 * i + a]);
         __syncthreads();     // every wave is done with its WaveLds: reuse the space
-        if (has_res) residual_tokens<GS>(sm, res_kv, nres, G);
+        if (has_res) bad_page |= !residual_tokens<KB, VB, GS>(p, sm, res_kv, nres, G, bh, append, flush, full);
         MergeLds<GS> &M = sm.u.merge;
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
@@ -722,7 +754,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             }
         }
     } else if (has_res) {
-        residual_tokens<GS>(sm, res_kv, nres, G);
+        bad_page |= !residual_tokens<KB, VB, GS>(p, sm, res_kv, nres, G, bh, append, flush, full);
     }
 
     // ---- this workgroup's merge: its waves' page states and, on the last split, the residual

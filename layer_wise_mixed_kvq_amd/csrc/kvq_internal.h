@@ -37,11 +37,14 @@ struct AppendParams {
 
 struct DecodeParams {
     const void *q;
-    const int32_t *seq_len;
+    const int32_t *seq_len;      // tokens attended (decode only; null with the fused append)
+    const int32_t *pos;          // fused append: position of the new token (attends pos + 1)
+    const uint16_t *k_new;       // fused append: bf16 [batch][H][128]
+    const uint16_t *v_new;
     const int32_t *block_table;
-    const void *pages;
-    const uint16_t *resid_k;
-    const uint16_t *resid_v;
+    void *pages;                 // written only by the fused append's page flush
+    uint16_t *resid_k;           // written only by the fused append (the new token's slot)
+    uint16_t *resid_v;
     float *out;
     float *lse;
     float *part_o;        // [batch][H][n_splits][G][128]
@@ -54,7 +57,7 @@ struct DecodeParams {
     int max_pages;
     int max_seq_len;
     int pages_per_split;
-    int n_splits;         // page splits + 1 residual slot, per (b, h)
+    int n_splits;         // page splits per (b, h)
 };
 
 // Workspace layout of kvq_decode_attn for (batch, H, G, n_splits).

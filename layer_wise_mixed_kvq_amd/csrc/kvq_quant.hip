@@ -8,121 +8,17 @@
 //   [KVTuner OpenReview discussion (paperhub.cn/paper/zDwipF6h06), reply to reviewer 1,
 //    section 4; reply to reviewer 2, section 2; reply to reviewer 3, section 1]
 //
-// One workgroup of 256 threads quantizes one page of one KV head:
-//   1. the 32 x 128 K and V tiles are staged in LDS as binary32 (coalesced 8/16-byte
-//      loads, 16 threads per 256-byte token row);
-//   2. threads 0..127 each reduce one key channel over the 32 tokens, threads 128..255
-//      each reduce one (token, 32-channel group) of the values -- every thread owns exactly
-//      one group, so the min/max needs no cross-thread reduction;
-//   3. each thread encodes its own 32 values (binary32 subtract and correctly rounded
-//      divide, round half to even, clamp) and writes the codes as bytes to LDS;
-//   4. all 256 threads pack the code bytes into the bit layout and store whole dwords.
+// One workgroup of 256 threads quantizes one page of one KV head: the 32 x 128 K and V
+// tiles are staged in LDS as binary32 (coalesced 8/16-byte loads, 16 threads per 256-byte
+// token row), then the page codec of kvq_codec.h encodes and packs them.
+#include "kvq_codec.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTileStride = kHeadDim + 1;   // padded row: column walks hit distinct banks
-
-struct QuantSmem {
-    float k[kGroup * kTileStride];
-    float v[kGroup * kTileStride];
-    uint8_t kcode[kGroup * kHeadDim];        // [token][channel]
-    uint8_t vcode[kHeadDim * kGroup];        // [channel][token]
-};
-
-// Codec of one 32-value group held by one thread.  Strict IEEE binary32: the compiler
-// must not contract or reassociate anything in here.
-template <int BITS>
-__device__ __forceinline__ void quant_group(const float *x, int stride, uint32_t &sz_word,
-                                            uint8_t *codes, int code_stride)
-{
-#pragma clang fp contract(off)
-    float v[kGroup];
-    float mn, mx;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) v[i] = x[i * stride] + 0.0f;   // -0 -> +0
-    mn = v[0];
-    mx = v[0];
-#pragma unroll
-    for (int i = 1; i < kGroup; ++i) {
-        mn = v[i] < mn ? v[i] : mn;
-        mx = v[i] > mx ? v[i] : mx;
-    }
-    constexpr float levels = static_cast<float>((1 << BITS) - 1);
-    const float s32 = (mx - mn) / levels;
-    const uint16_t s16 = float_to_half_bits(s32);
-    const uint16_t z16 = float_to_half_bits(mn);
-    const float s = half_bits_to_float(s16);
-    const float z = half_bits_to_float(z16);
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-        uint32_t code = 0;
-        if (s != 0.0f) {
-            const float q = (v[i] - z) / s;
-            float r = __builtin_rintf(q);
-            r = r < 0.0f ? 0.0f : r;
-            r = r > levels ? levels : r;
-            code = static_cast<uint32_t>(r);
-        }
-        codes[i * code_stride] = static_cast<uint8_t>(code);
-    }
-    sz_word = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
-}
-
-// Quantize the staged tiles of one page-head into `dst` (global).  All 256 threads call.
-template <int KB, int VB>
-__device__ void quantize_page(QuantSmem &sm, uint8_t *__restrict__ dst)
-{
-    using P = PageLayout<KB, VB>;
-    const int tid = threadIdx.x;
-    uint32_t *dst32 = reinterpret_cast<uint32_t *>(dst);
-    if (tid < kHeadDim) {
-        const int c = tid;
-        uint32_t w;
-        quant_group<KB>(&sm.k[c], kTileStride, w, &sm.kcode[c], kHeadDim);
-        dst32[P::kKSz / 4 + c] = w;
-    } else {
-        const int t = (tid - kHeadDim) & (kGroup - 1);
-        const int j = (tid - kHeadDim) >> 5;
-        uint32_t w;
-        quant_group<VB>(&sm.v[t * kTileStride + kGroup * j], 1, w, &sm.vcode[(kGroup * j) * kGroup + t],
-                        kGroup);
-        dst32[P::kVSz / 4 + kValueGroups * t + j] = w;
-    }
-    __syncthreads();
-    // K codes: dword d of the section holds 32/KB consecutive channels of one token row
-    constexpr int kPerWord = 32 / KB;
-    for (int d = tid; d < 128 * KB; d += kThreads) {
-        const int t = d / (4 * KB);
-        const int c0 = (d % (4 * KB)) * kPerWord;
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < kPerWord; ++i) w |= static_cast<uint32_t>(sm.kcode[t * kHeadDim + c0 + i]) << (i * KB);
-        dst32[P::kKCodes / 4 + d] = w;
-    }
-    // V codes: 64 chunks of 2*VB words; chunk 16q + r holds tokens 8q..8q+7 of channels
-    // r, r+16, ..., r+112.  Word dw of a chunk holds, in each 16-bit half hh, the codes of
-    // k = dw*n .. dw*n + n-1 (n = 16/VB), k = 4*(c/16) + (t%4), token t = 8q + (t%4) + 4hh.
-    constexpr int n = 16 / VB;
-    for (int d = tid; d < 128 * VB; d += kThreads) {
-        const int u = d / (2 * VB), dw = d % (2 * VB);
-        const int q = u >> 4, r = u & 15;
-        uint32_t w = 0;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int kk = 0; kk < n; ++kk) {
-                const int k = dw * n + kk;
-                const int t = 8 * q + (k & 3) + 4 * hh, c = 16 * (k >> 2) + r;
-                w |= static_cast<uint32_t>(sm.vcode[c * kGroup + t]) << (16 * hh + VB * kk);
-            }
-        }
-        dst32[P::kVCodes / 4 + d] = w;
-    }
-}
+constexpr int kThreads = kCodecThreads;
 
 template <typename SrcT>
 struct Src;

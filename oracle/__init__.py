@@ -70,17 +70,17 @@ def lib() -> ctypes.CDLL:
         L.orc_quant_group.restype = ci
         L.orc_head_page_bytes.argtypes = [ci, ci]
         L.orc_head_page_bytes.restype = ctypes.c_size_t
-        L.orc_pack_page.argtypes = [f32p, f32p, ci, ci, ci, u8p]
-        L.orc_pack_page.restype = ci
-        L.orc_dequant_page.argtypes = [u8p, ci, ci, f64p, f64p]
-        L.orc_dequant_page.restype = ci
-        L.orc_pack.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, i32p, i32p, ci, u8p, u16p, u16p]
-        L.orc_pack.restype = ci
-        L.orc_append.argtypes = [ci, ci, ci, ci, u16p, u16p, i32p, i32p, ci, u8p, u16p, u16p]
-        L.orc_append.restype = ci
-        L.orc_decode_attn.argtypes = [ci, ci, ci, ci, ci, ci, vp, i32p, i32p, ci, u8p, u16p, u16p,
-                                      f64p, f64p]
-        L.orc_decode_attn.restype = ci
+        L.orc_pack_page_m.argtypes = [f32p, f32p, ci, ci, ci, ci, u8p]
+        L.orc_pack_page_m.restype = ci
+        L.orc_dequant_page_m.argtypes = [u8p, ci, ci, ci, f64p, f64p]
+        L.orc_dequant_page_m.restype = ci
+        L.orc_pack_m.argtypes = [ci, ci, ci, ci, ci, ci, ci, vp, vp, i32p, i32p, ci, u8p, u16p, u16p]
+        L.orc_pack_m.restype = ci
+        L.orc_append_m.argtypes = [ci, ci, ci, ci, ci, u16p, u16p, i32p, i32p, ci, u8p, u16p, u16p]
+        L.orc_append_m.restype = ci
+        L.orc_decode_attn_m.argtypes = [ci, ci, ci, ci, ci, ci, ci, vp, i32p, i32p, ci, u8p, u16p, u16p,
+                                        f64p, f64p]
+        L.orc_decode_attn_m.restype = ci
         _lib = L
     return _lib
 
@@ -131,23 +131,26 @@ def head_page_bytes(kb: int, vb: int) -> int:
     return int(lib().orc_head_page_bytes(kb, vb))
 
 
-def pack_page(k_tile: np.ndarray, v_tile: np.ndarray, kb: int, vb: int) -> np.ndarray:
+KMODE_CHANNEL, KMODE_TOKEN = 0, 1   # keys per channel over 32 tokens / per token over 32 channels
+
+
+def pack_page(k_tile: np.ndarray, v_tile: np.ndarray, kb: int, vb: int, kmode: int = KMODE_CHANNEL) -> np.ndarray:
     """Quantize one 32x128 fp32 K tile and V tile into one packed page (uint8)."""
     k = np.ascontiguousarray(k_tile, dtype=np.float32).reshape(GROUP, HEAD_DIM)
     v = np.ascontiguousarray(v_tile, dtype=np.float32).reshape(GROUP, HEAD_DIM)
     out = np.zeros(head_page_bytes(kb, vb), dtype=np.uint8)
-    _check(lib().orc_pack_page(_ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), HEAD_DIM, kb, vb,
-                               _ptr(out, ctypes.c_uint8)), "pack_page")
+    _check(lib().orc_pack_page_m(_ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), HEAD_DIM, kb, vb, kmode,
+                                 _ptr(out, ctypes.c_uint8)), "pack_page")
     return out
 
 
-def dequant_page(page: np.ndarray, kb: int, vb: int):
+def dequant_page(page: np.ndarray, kb: int, vb: int, kmode: int = KMODE_CHANNEL):
     """Packed page -> (K, V) float64 [32][128]."""
     p = np.ascontiguousarray(page, dtype=np.uint8)
     k = np.zeros((GROUP, HEAD_DIM), dtype=np.float64)
     v = np.zeros((GROUP, HEAD_DIM), dtype=np.float64)
-    _check(lib().orc_dequant_page(_ptr(p, ctypes.c_uint8), kb, vb, _ptr(k, ctypes.c_double),
-                                  _ptr(v, ctypes.c_double)), "dequant_page")
+    _check(lib().orc_dequant_page_m(_ptr(p, ctypes.c_uint8), kb, vb, kmode, _ptr(k, ctypes.c_double),
+                                    _ptr(v, ctypes.c_double)), "dequant_page")
     return k, v
 
 
@@ -166,7 +169,7 @@ def _src_kind(a: np.ndarray) -> int:
 
 
 def pack(kb: int, vb: int, k_src: np.ndarray, v_src: np.ndarray, seq_len, block_table,
-         pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray) -> None:
+         pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL) -> None:
     """Prefill quantize-on-write; k_src, v_src are [B][T][H][128]; updates in place."""
     B, T, H, D = k_src.shape
     assert D == HEAD_DIM and v_src.shape == k_src.shape and v_src.dtype == k_src.dtype
@@ -175,14 +178,14 @@ def pack(kb: int, vb: int, k_src: np.ndarray, v_src: np.ndarray, seq_len, block_
     v_src = np.ascontiguousarray(v_src)
     sl = np.ascontiguousarray(seq_len, dtype=np.int32)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
-    _check(lib().orc_pack(kb, vb, H, B, T, kind, k_src.ctypes.data, v_src.ctypes.data,
+    _check(lib().orc_pack_m(kb, vb, kmode, H, B, T, kind, k_src.ctypes.data, v_src.ctypes.data,
                           _ptr(sl, ctypes.c_int32), _ptr(bt, ctypes.c_int32), bt.shape[1],
                           _ptr(pages, ctypes.c_uint8), _ptr(resid_k, ctypes.c_uint16),
                           _ptr(resid_v, ctypes.c_uint16)), "pack")
 
 
 def append(kb: int, vb: int, k_new: np.ndarray, v_new: np.ndarray, pos, block_table,
-           pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray) -> None:
+           pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL) -> None:
     """Decode-time write of one bf16 token per sequence ([B][H][128] uint16); in place."""
     B, H, D = k_new.shape
     assert D == HEAD_DIM and k_new.dtype == np.uint16 and v_new.dtype == np.uint16
@@ -190,14 +193,14 @@ def append(kb: int, vb: int, k_new: np.ndarray, v_new: np.ndarray, pos, block_ta
     vn = np.ascontiguousarray(v_new)
     p = np.ascontiguousarray(pos, dtype=np.int32)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
-    _check(lib().orc_append(kb, vb, H, B, _ptr(kn, ctypes.c_uint16), _ptr(vn, ctypes.c_uint16),
+    _check(lib().orc_append_m(kb, vb, kmode, H, B, _ptr(kn, ctypes.c_uint16), _ptr(vn, ctypes.c_uint16),
                             _ptr(p, ctypes.c_int32), _ptr(bt, ctypes.c_int32), bt.shape[1],
                             _ptr(pages, ctypes.c_uint8), _ptr(resid_k, ctypes.c_uint16),
                             _ptr(resid_v, ctypes.c_uint16)), "append")
 
 
 def decode_attn(kb: int, vb: int, n_kv_heads: int, q: np.ndarray, seq_len, block_table,
-                pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray):
+                pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL):
     """binary64 decode attention; q is [B][Hq][128] (bf16 bits as uint16, or float32).
     Returns (out float64 [B][Hq][128], lse float64 [B][Hq])."""
     B, Hq, D = q.shape
@@ -208,7 +211,7 @@ def decode_attn(kb: int, vb: int, n_kv_heads: int, q: np.ndarray, seq_len, block
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     out = np.zeros((B, Hq, D), dtype=np.float64)
     lse = np.zeros((B, Hq), dtype=np.float64)
-    _check(lib().orc_decode_attn(kb, vb, Hq, n_kv_heads, B, kind, q.ctypes.data,
+    _check(lib().orc_decode_attn_m(kb, vb, kmode, Hq, n_kv_heads, B, kind, q.ctypes.data,
                                  _ptr(sl, ctypes.c_int32), _ptr(bt, ctypes.c_int32), bt.shape[1],
                                  _ptr(pages, ctypes.c_uint8), _ptr(resid_k, ctypes.c_uint16),
                                  _ptr(resid_v, ctypes.c_uint16), _ptr(out, ctypes.c_double),

@@ -211,6 +211,38 @@ static size_t vcode_bit(int t, int c, int vb)
     return chunk_bits + 32 * (size_t)(k / n) + 16 * (size_t)hh + (size_t)vb * (k % n);
 }
 
+/* Key modes.  KMODE_CHANNEL: one key group per channel over the page's 32 tokens; token
+ * row t holds channel c at bit c*kb; K s/z word c.  KMODE_TOKEN: one key group per
+ * (token, 32 consecutive channels), like the values; K s/z word 4t + j for channels
+ * 32j .. 32j+31, and the row's channels are permuted as follows.
+ *   [When should you use mixed-precision KV caching ... (machinoai.in); KVTuner OpenReview
+ *    discussion, reply to reviewer 1, section 4 (per-token asymmetric keys)]
+ * Per-token key row layout: the row's 16*kb bytes are four chunks of 4*kb bytes; slot s of
+ * chunk a (bits s*kb .. s*kb + kb-1 of the chunk) holds channel
+ *     32*(k / 4) + 8*a + 2*(k % 4) + hh,   with n = 16/kb, x = s / (2n),
+ *     hh = (s / n) mod 2, p = s mod n, k = x*n + p.
+ * So chunk a holds channels 32J + 8a .. 32J + 8a + 7 of every key group J, and the two
+ * channels 32J + 8a + 2i and 32J + 8a + 2i + 1 sit at the same position of the two 16-bit
+ * halves of one 32-bit word. */
+enum { KMODE_CHANNEL = 0, KMODE_TOKEN = 1 };
+
+static int kslot_channel(int a, int slot, int kb)
+{
+    int n = 16 / kb;
+    int x = slot / (2 * n), hh = (slot / n) % 2, p = slot % n;
+    int k = x * n + p;
+    return 32 * (k / 4) + 8 * a + 2 * (k % 4) + hh;
+}
+
+/* bit offset, inside a per-token key row, of channel c */
+static size_t ktok_bit(int c, int kb)
+{
+    for (int a = 0; a < 4; ++a)
+        for (int slot = 0; slot < 32; ++slot)
+            if (kslot_channel(a, slot, kb) == c) return (size_t)(a * 32 + slot) * kb;
+    return (size_t)-1;
+}
+
 static void put_code_at(uint8_t *base, size_t bit, unsigned code)
 {
     base[bit / 8] |= (uint8_t)(code << (bit % 8));
@@ -245,18 +277,29 @@ static uint32_t get_u32(const uint8_t *p)
 
 /* Quantize one page: k and v point at token 0, channel 0 of a 32 x 128 fp32 tile whose
  * consecutive tokens are `tok_stride` floats apart. */
-int orc_pack_page(const float *k, const float *v, int tok_stride, int kb, int vb, uint8_t *dst)
+int orc_pack_page_m(const float *k, const float *v, int tok_stride, int kb, int vb, int kmode, uint8_t *dst)
 {
-    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
     memset(dst, 0, orc_head_page_bytes(kb, vb));
     uint8_t codes[ORC_G];
     uint16_t s16, z16;
-    /* keys: one group per channel, over the page's 32 tokens */
-    for (int c = 0; c < ORC_D; ++c) {
-        orc_quant_group(k + c, tok_stride, kb, &s16, &z16, codes);
+    if (kmode == KMODE_CHANNEL) {
+        /* keys: one group per channel, over the page's 32 tokens */
+        for (int c = 0; c < ORC_D; ++c) {
+            orc_quant_group(k + c, tok_stride, kb, &s16, &z16, codes);
+            for (int t = 0; t < ORC_G; ++t)
+                put_code(dst + off_kcodes(kb, vb) + (size_t)t * 16 * kb, c, kb, codes[t]);
+            put_u32(dst + off_ksz(kb, vb) + 4 * (size_t)c, (uint32_t)s16 | (uint32_t)z16 << 16);
+        }
+    } else {
+        /* keys: one group per (token, 32 consecutive channels) */
         for (int t = 0; t < ORC_G; ++t)
-            put_code(dst + off_kcodes(kb, vb) + (size_t)t * 16 * kb, c, kb, codes[t]);
-        put_u32(dst + off_ksz(kb, vb) + 4 * (size_t)c, (uint32_t)s16 | (uint32_t)z16 << 16);
+            for (int j = 0; j < ORC_D / ORC_G; ++j) {
+                orc_quant_group(k + (size_t)t * tok_stride + 32 * j, 1, kb, &s16, &z16, codes);
+                for (int i = 0; i < ORC_G; ++i)
+                    put_code_at(dst + off_kcodes(kb, vb) + (size_t)t * 16 * kb, ktok_bit(32 * j + i, kb), codes[i]);
+                put_u32(dst + off_ksz(kb, vb) + 4 * (size_t)(4 * t + j), (uint32_t)s16 | (uint32_t)z16 << 16);
+            }
     }
     /* values: one group per (token, 32 consecutive channels) */
     for (int t = 0; t < ORC_G; ++t) {
@@ -271,17 +314,24 @@ int orc_pack_page(const float *k, const float *v, int tok_stride, int kb, int vb
     return 0;
 }
 
+int orc_pack_page(const float *k, const float *v, int tok_stride, int kb, int vb, uint8_t *dst)
+{
+    return orc_pack_page_m(k, v, tok_stride, kb, vb, KMODE_CHANNEL, dst);
+}
+
 /* Decode one page into binary64 K and V tiles [32][128].  code * s + z is exact in
  * binary64 (an 8-bit integer times a binary16 value plus a binary16 value). */
-int orc_dequant_page(const uint8_t *src, int kb, int vb, double *k, double *v)
+int orc_dequant_page_m(const uint8_t *src, int kb, int vb, int kmode, double *k, double *v)
 {
-    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
-    for (int c = 0; c < ORC_D; ++c) {
-        uint32_t w = get_u32(src + off_ksz(kb, vb) + 4 * (size_t)c);
-        double s = orc_f16_to_f32((uint16_t)(w & 0xffffu));
-        double z = orc_f16_to_f32((uint16_t)(w >> 16));
-        for (int t = 0; t < ORC_G; ++t) {
-            unsigned code = get_code(src + off_kcodes(kb, vb) + (size_t)t * 16 * kb, c, kb);
+    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
+    for (int t = 0; t < ORC_G; ++t) {
+        const uint8_t *row = src + off_kcodes(kb, vb) + (size_t)t * 16 * kb;
+        for (int c = 0; c < ORC_D; ++c) {
+            size_t widx = kmode == KMODE_CHANNEL ? (size_t)c : (size_t)(4 * t + c / 32);
+            uint32_t w = get_u32(src + off_ksz(kb, vb) + 4 * widx);
+            double s = orc_f16_to_f32((uint16_t)(w & 0xffffu));
+            double z = orc_f16_to_f32((uint16_t)(w >> 16));
+            unsigned code = kmode == KMODE_CHANNEL ? get_code(row, c, kb) : get_code_at(row, ktok_bit(c, kb), kb);
             k[t * ORC_D + c] = (double)code * s + z;
         }
     }
@@ -295,6 +345,11 @@ int orc_dequant_page(const uint8_t *src, int kb, int vb, double *k, double *v)
         }
     }
     return 0;
+}
+
+int orc_dequant_page(const uint8_t *src, int kb, int vb, double *k, double *v)
+{
+    return orc_dequant_page_m(src, kb, vb, KMODE_CHANNEL, k, v);
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -315,12 +370,12 @@ static uint16_t src_to_bf16(const void *src, int is_bf16, size_t i)
  * k_src / v_src [batch][max_tokens][H][128] (bf16 or fp32).  Full 32-token groups go to
  * the pages named by the block table; the last seq_len mod 32 tokens go, as bf16, to
  * residual slot t mod 32 of resid_k / resid_v [batch][H][32][128]. */
-int orc_pack(int kb, int vb, int H, int batch, int max_tokens, int src_is_bf16,
-             const void *k_src, const void *v_src, const int32_t *seq_len,
-             const int32_t *block_table, int max_pages,
-             uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+int orc_pack_m(int kb, int vb, int kmode, int H, int batch, int max_tokens, int src_is_bf16,
+               const void *k_src, const void *v_src, const int32_t *seq_len,
+               const int32_t *block_table, int max_pages,
+               uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
 {
-    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
     const size_t hp = orc_head_page_bytes(kb, vb);
     static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
     for (int b = 0; b < batch; ++b) {
@@ -336,7 +391,7 @@ int orc_pack(int kb, int vb, int H, int batch, int max_tokens, int src_is_bf16,
                         tv[t * ORC_D + c] = src_elem(v_src, src_is_bf16, i);
                     }
                 int32_t phys = block_table[(size_t)b * max_pages + g];
-                orc_pack_page(tk, tv, ORC_D, kb, vb, pages + ((size_t)phys * H + h) * hp);
+                orc_pack_page_m(tk, tv, ORC_D, kb, vb, kmode, pages + ((size_t)phys * H + h) * hp);
             }
             for (int t = full * ORC_G; t < L; ++t)
                 for (int c = 0; c < ORC_D; ++c) {
@@ -354,11 +409,11 @@ int orc_pack(int kb, int vb, int H, int batch, int max_tokens, int src_is_bf16,
  * the write).  The token goes to residual slot pos mod 32; when that slot is 31 the 32
  * residual tokens form a full group and are quantized into page pos / 32.
  * k_new / v_new are bf16 [batch][H][128]. */
-int orc_append(int kb, int vb, int H, int batch, const uint16_t *k_new, const uint16_t *v_new,
-               const int32_t *pos, const int32_t *block_table, int max_pages,
-               uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+int orc_append_m(int kb, int vb, int kmode, int H, int batch, const uint16_t *k_new, const uint16_t *v_new,
+                 const int32_t *pos, const int32_t *block_table, int max_pages,
+                 uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
 {
-    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
     const size_t hp = orc_head_page_bytes(kb, vb);
     static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
     for (int b = 0; b < batch; ++b) {
@@ -378,7 +433,7 @@ int orc_append(int kb, int vb, int H, int batch, const uint16_t *k_new, const ui
                     tv[i] = orc_bf16_to_f32(rv[i]);
                 }
                 int32_t phys = block_table[(size_t)b * max_pages + p / ORC_G];
-                orc_pack_page(tk, tv, ORC_D, kb, vb, pages + ((size_t)phys * H + h) * hp);
+                orc_pack_page_m(tk, tv, ORC_D, kb, vb, kmode, pages + ((size_t)phys * H + h) * hp);
             }
         }
     }
@@ -392,12 +447,12 @@ int orc_append(int kb, int vb, int H, int batch, const uint16_t *k_new, const ui
  *   lse = m + ln l,  out_c = sum_j exp(s_j - m) v_jc / l.
  * q is [batch][Hq][128] (bf16 or fp32); out is [batch][Hq][128]; lse is [batch][Hq]
  * (may be NULL). */
-int orc_decode_attn(int kb, int vb, int Hq, int H, int batch, int q_is_bf16, const void *q,
-                    const int32_t *seq_len, const int32_t *block_table, int max_pages,
-                    const uint8_t *pages, const uint16_t *resid_k, const uint16_t *resid_v,
-                    double *out, double *lse)
+int orc_decode_attn_m(int kb, int vb, int kmode, int Hq, int H, int batch, int q_is_bf16, const void *q,
+                      const int32_t *seq_len, const int32_t *block_table, int max_pages,
+                      const uint8_t *pages, const uint16_t *resid_k, const uint16_t *resid_v,
+                      double *out, double *lse)
 {
-    if (!valid_bits(kb) || !valid_bits(vb)) return 1;
+    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
     if (H <= 0 || Hq % H != 0) return 3;
     const int G = Hq / H;
     const size_t hp = orc_head_page_bytes(kb, vb);
@@ -413,8 +468,8 @@ int orc_decode_attn(int kb, int vb, int Hq, int H, int batch, int q_is_bf16, con
             /* this head's keys and values for all L tokens, as exact binary64 */
             for (int g = 0; g < full; ++g) {
                 int32_t phys = block_table[(size_t)b * max_pages + g];
-                orc_dequant_page(pages + ((size_t)phys * H + h) * hp, kb, vb,
-                                 K + (size_t)g * ORC_G * ORC_D, V + (size_t)g * ORC_G * ORC_D);
+                orc_dequant_page_m(pages + ((size_t)phys * H + h) * hp, kb, vb, kmode,
+                                   K + (size_t)g * ORC_G * ORC_D, V + (size_t)g * ORC_G * ORC_D);
             }
             const uint16_t *rk = resid_k + ((size_t)b * H + h) * ORC_G * ORC_D;
             const uint16_t *rv = resid_v + ((size_t)b * H + h) * ORC_G * ORC_D;
@@ -449,4 +504,31 @@ int orc_decode_attn(int kb, int vb, int Hq, int H, int batch, int q_is_bf16, con
         free(K); free(V); free(s);
     }
     return 0;
+}
+
+/* per-channel-key entry points (the library's default key mode) */
+int orc_pack(int kb, int vb, int H, int batch, int max_tokens, int src_is_bf16,
+             const void *k_src, const void *v_src, const int32_t *seq_len,
+             const int32_t *block_table, int max_pages,
+             uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+{
+    return orc_pack_m(kb, vb, KMODE_CHANNEL, H, batch, max_tokens, src_is_bf16, k_src, v_src, seq_len,
+                      block_table, max_pages, pages, resid_k, resid_v);
+}
+
+int orc_append(int kb, int vb, int H, int batch, const uint16_t *k_new, const uint16_t *v_new,
+               const int32_t *pos, const int32_t *block_table, int max_pages,
+               uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+{
+    return orc_append_m(kb, vb, KMODE_CHANNEL, H, batch, k_new, v_new, pos, block_table, max_pages,
+                        pages, resid_k, resid_v);
+}
+
+int orc_decode_attn(int kb, int vb, int Hq, int H, int batch, int q_is_bf16, const void *q,
+                    const int32_t *seq_len, const int32_t *block_table, int max_pages,
+                    const uint8_t *pages, const uint16_t *resid_k, const uint16_t *resid_v,
+                    double *out, double *lse)
+{
+    return orc_decode_attn_m(kb, vb, KMODE_CHANNEL, Hq, H, batch, q_is_bf16, q, seq_len, block_table, max_pages,
+                             pages, resid_k, resid_v, out, lse);
 }

@@ -51,6 +51,10 @@ CONFIGS = {
     "pack": dict(workload="prefill pack, llama3.1-8b shape C3.25, 32768 tokens, batch 1 (32 layers)",
                  pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=1, context=32768, n_outliers=3,
                  seed=20250206),
+    "ktoken": dict(workload="llama3.1-8b-shape C3.25 decode step with per-token keys in every layer "
+                            "(append + attention, 32 layers)",
+                   pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=16, context=4096, n_outliers=3,
+                   seed=20250204, k_mode=1),
     "copy": dict(workload="streaming copy: 1 GiB int32 read + 1 GiB written (torch bitwise_not)"),
     "sweep": dict(workload="uniform-pair sweep, llama3.1-8b shape, 32 layers: decode step tokens/s per table "
                            "relative to KV8 at the (batch, input length) points of the pages' throughput table "
@@ -128,7 +132,8 @@ class DecodeStack:
         self.cfg = cfg
         self.kvq = kvq
         pairs = cfg["pairs"]
-        self.model = kvq.Model(pairs, cfg["n_q_heads"], cfg["n_kv_heads"])
+        self.k_mode = cfg.get("k_mode", 0)       # 0: per-channel keys, 1: per-token keys
+        self.model = kvq.Model([(kb, vb, self.k_mode) for kb, vb in pairs], cfg["n_q_heads"], cfg["n_kv_heads"])
         B, H = cfg["batch"], cfg["n_kv_heads"]
         seed = cfg["seed"]
         if "ragged" in cfg:
@@ -282,11 +287,12 @@ def cpu_baseline_decode(cfg, stack, n_seq):
             kn = synth.fill(seed, synth.KIND_K_NEW, l, 1, 1, H, b0=b, chan_mult=cm).view(1, H, 128)
             vn = synth.fill(seed, synth.KIND_V_NEW, l, 1, 1, H, b0=b).view(1, H, 128)
             q = synth.fill(seed, synth.KIND_Q, l, 1, 1, Hq, b0=b).view(1, Hq, 128)
+            km = cfg.get("k_mode", 0)
             pages, rk, rv = orc.new_cache(kb, vb, H, 1, maxp)
-            orc.pack(kb, vb, bits(k), bits(v), [C], bt, pages, rk, rv)
+            orc.pack(kb, vb, bits(k), bits(v), [C], bt, pages, rk, rv, kmode=km)
             t0 = time.perf_counter()
-            orc.append(kb, vb, bits(kn), bits(vn), [C], bt, pages, rk, rv)
-            orc.decode_attn(kb, vb, H, bits(q), [C + 1], bt, pages, rk, rv)
+            orc.append(kb, vb, bits(kn), bits(vn), [C], bt, pages, rk, rv, kmode=km)
+            orc.decode_attn(kb, vb, H, bits(q), [C + 1], bt, pages, rk, rv, kmode=km)
             t_total += time.perf_counter() - t0
             attended += C + 1
     return t_total, attended
@@ -398,7 +404,8 @@ def main():
         "config": {"workload": cfg["workload"], "batch": stack.B, "context": stack.C,
                    "attended_tokens": stack.L, "mean_attended_tokens": float(stack.attend.mean()), "layers": n_layers, "n_q_heads": stack.Hq,
                    "n_kv_heads": stack.H, "head_dim": 128, "equiv_bits": kvq.kvq_equiv_bits(stack.model),
-                   "graph": not args.no_graph, "fused_append": with_append and not args.unfused},
+                   "graph": not args.no_graph, "fused_append": with_append and not args.unfused,
+                   "keys": "per-token" if stack.k_mode else "per-channel"},
         "packed_kv_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "packed_kv_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "step_alg_bytes": step_bytes,

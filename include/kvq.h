@@ -33,13 +33,19 @@
  *     s, z = s16, z16 widened to binary32
  *     code_i = clamp(round_half_even((x_i - z) / s), 0, 2^b - 1), all 0 when s == 0
  *     dequantized value = code * s + z
- *   Keys: one group per (page, KV head, channel) over the page's 32 tokens.
+ *   Keys, per-channel mode: one group per (page, KV head, channel) over the page's 32
+ *   tokens.  Keys, per-token mode: one group per (token, KV head, 32 consecutive channels).
  *   Values: one group per (token, KV head, 32 consecutive channels).
  *
  *   One page = 32 consecutive tokens of one sequence for all KV heads of one layer.
  *   A layer's pool is [physical page][KV head][head_page], head_page = 512*(kb+vb+2) bytes:
- *     +0              K codes, token-major: row t (16*kb bytes), channel c at bit c*kb
- *     +512*kb         K scale/zero: 128 x u32, word c = s16 | z16 << 16
+ *     +0              K codes, token-major: row t (16*kb bytes).  Per-channel mode:
+ *                     channel c at bit c*kb.  Per-token mode: the row is four chunks of
+ *                     4*kb bytes and slot s of chunk a (bit s*kb of the chunk) holds
+ *                     channel 32*(k/4) + 8*a + 2*(k%4) + hh, where n = 16/kb,
+ *                     hh = (s/n)%2, k = (s/(2n))*n + s%n
+ *     +512*kb         K scale/zero: 128 x u32 = s16 | z16 << 16; per-channel mode word c,
+ *                     per-token mode word 4*t + j (channels 32j..32j+31)
  *     +512*kb+512     V codes: 64 chunks of 8*vb bytes; chunk 16*q + r holds tokens
  *                     8q..8q+7 of channels r, r+16, ..., r+112; inside it, with
  *                     i = t%8, j = i%4, k = 4*(c/16) + j, n = 16/vb, the code of
@@ -89,8 +95,19 @@ typedef enum kvq_status {
 
 typedef enum kvq_dtype { KVQ_BF16 = 0, KVQ_F32 = 1 } kvq_dtype;
 
+/* Key quantization modes.  KVQ_KEYS_PER_CHANNEL (the default): one key group per channel
+ * over a page's 32 tokens -- keys carry channel-wise outliers.  KVQ_KEYS_PER_TOKEN: one
+ * key group per (token, 32 consecutive channels), the rule the values use.  The pages
+ * compare the two modes and find different Pareto-optimal pairs for each.
+ *   [Mixed-precision KV-cache quantization per-layer sensitivity (llms-explorer.com), Facts]
+ *   [KVTuner OpenReview discussion, reply to reviewer 1, section 4] */
+#define KVQ_KEYS_PER_CHANNEL 0
+#define KVQ_KEYS_PER_TOKEN 1
+
 /* The per-layer precision table and the attention shape.  k_bits / v_bits are HOST
- * arrays of n_layers entries, each 2, 4 or 8. */
+ * arrays of n_layers entries, each 2, 4 or 8.  k_mode is a HOST array of n_layers key
+ * modes (KVQ_KEYS_PER_CHANNEL / KVQ_KEYS_PER_TOKEN), or NULL for per-channel keys in every
+ * layer. */
 typedef struct kvq_model {
     int32_t n_layers;
     int32_t n_q_heads;
@@ -98,6 +115,7 @@ typedef struct kvq_model {
     int32_t head_dim;          /* must be 128 */
     const uint8_t *k_bits;
     const uint8_t *v_bits;
+    const uint8_t *k_mode;     /* optional, see above */
 } kvq_model;
 
 /* One layer's cache (all device pointers). */

@@ -22,23 +22,31 @@ from ._native import KVQ_BF16, KVQ_F32, KvqError, KvqLayerCache, KvqModel, check
 HEAD_DIM = 128
 GROUP = 32
 
-__all__ = ["Model", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
+__all__ = ["Model", "KEYS_PER_CHANNEL", "KEYS_PER_TOKEN", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_head_page_bytes",
            "kvq_page_bytes", "kvq_equiv_bits", "kvq_format_version", "lib"]
 
 
-class Model:
-    """Per-layer (key bits, value bits) table plus the attention shape (kvq_model)."""
+KEYS_PER_CHANNEL, KEYS_PER_TOKEN = 0, 1
 
-    def __init__(self, pairs: Sequence[tuple[int, int]], n_q_heads: int, n_kv_heads: int,
-                 head_dim: int = HEAD_DIM):
-        self.pairs = [(int(k), int(v)) for k, v in pairs]
+
+class Model:
+    """Per-layer table plus the attention shape (kvq_model).  Each entry of `pairs` is
+    (key bits, value bits) for per-channel keys, or (key bits, value bits, key mode) with
+    key mode "channel" / "token" (or KEYS_PER_CHANNEL / KEYS_PER_TOKEN)."""
+
+    def __init__(self, pairs: Sequence[tuple], n_q_heads: int, n_kv_heads: int, head_dim: int = HEAD_DIM):
+        modes = {"channel": KEYS_PER_CHANNEL, "token": KEYS_PER_TOKEN, KEYS_PER_CHANNEL: KEYS_PER_CHANNEL,
+                 KEYS_PER_TOKEN: KEYS_PER_TOKEN}
+        self.pairs = [(int(e[0]), int(e[1])) for e in pairs]
+        self.k_modes = [modes[e[2]] if len(e) > 2 else KEYS_PER_CHANNEL for e in pairs]
         n = len(self.pairs)
         self._kb = (ctypes.c_uint8 * max(n, 1))(*[k for k, _ in self.pairs])
         self._vb = (ctypes.c_uint8 * max(n, 1))(*[v for _, v in self.pairs])
-        self.c = KvqModel(n, n_q_heads, n_kv_heads, head_dim,
-                          ctypes.cast(self._kb, ctypes.POINTER(ctypes.c_uint8)),
-                          ctypes.cast(self._vb, ctypes.POINTER(ctypes.c_uint8)))
+        self._km = (ctypes.c_uint8 * max(n, 1))(*self.k_modes)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        self.c = KvqModel(n, n_q_heads, n_kv_heads, head_dim, ctypes.cast(self._kb, u8p),
+                          ctypes.cast(self._vb, u8p), ctypes.cast(self._km, u8p))
         self.n_layers, self.n_q_heads, self.n_kv_heads, self.head_dim = n, n_q_heads, n_kv_heads, head_dim
 
     @property

@@ -20,7 +20,8 @@ EXPORTED = ("kvq_status_str", "kvq_format_version", "kvq_head_page_bytes", "kvq_
 class KvqModel(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("k_bits", ctypes.POINTER(ctypes.c_uint8)), ("v_bits", ctypes.POINTER(ctypes.c_uint8))]
+                ("k_bits", ctypes.POINTER(ctypes.c_uint8)), ("v_bits", ctypes.POINTER(ctypes.c_uint8)),
+                ("k_mode", ctypes.POINTER(ctypes.c_uint8))]
 
 
 class KvqLayerCache(ctypes.Structure):

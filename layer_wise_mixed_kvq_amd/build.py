@@ -9,10 +9,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_quant.hip", "kvq_decode.hip"]
+# (source, extra flags): the decode kernels build in one translation unit per key bit width
+UNITS = [("kvq_api.hip", []), ("kvq_quant.hip", []), ("kvq_decode.hip", ["-DKVQ_DECODE_COMMON"]),
+         ("kvq_decode.hip", ["-DKVQ_DECODE_KB=2"]), ("kvq_decode.hip", ["-DKVQ_DECODE_KB=4"]),
+         ("kvq_decode.hip", ["-DKVQ_DECODE_KB=8"])]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions anywhere in this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in ordinary VGPRs: the decode kernel rescales them with VALU ops,
@@ -22,15 +25,33 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = ["hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+def _compile(unit, obj, verbose):
+    src, extra = unit
+    cmd = ["hipcc", *HIPCC_FLAGS, "-c", *extra, "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libkvq.so")
+        raise RuntimeError(f"hipcc failed on {src} {' '.join(extra)}")
     if verbose:
         sys.stderr.write(res.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every unit for gfx950 (in parallel) and link libkvq.so in-tree."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, f"unit{i}.o") for i in range(len(UNITS))]
+    workers = max(1, min(len(UNITS), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda a: _compile(*a, verbose), [(u, o) for u, o in zip(UNITS, objs)]))
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("linking libkvq.so failed")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

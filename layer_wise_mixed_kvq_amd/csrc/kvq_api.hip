@@ -24,10 +24,15 @@ kvq_status check_model(const kvq_model *m)
     if (m->n_q_heads % m->n_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
     if (m->n_q_heads / m->n_kv_heads > kvq::decode_max_g()) return KVQ_ERR_UNSUPPORTED;
     if (m->n_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
-    for (int l = 0; l < m->n_layers; ++l)
+    for (int l = 0; l < m->n_layers; ++l) {
         if (!valid_bits(m->k_bits[l]) || !valid_bits(m->v_bits[l])) return KVQ_ERR_UNSUPPORTED;
+        if (m->k_mode && m->k_mode[l] != KVQ_KEYS_PER_CHANNEL && m->k_mode[l] != KVQ_KEYS_PER_TOKEN)
+            return KVQ_ERR_UNSUPPORTED;
+    }
     return KVQ_OK;
 }
+
+int key_mode(const kvq_model *m, int layer) { return m->k_mode ? m->k_mode[layer] : KVQ_KEYS_PER_CHANNEL; }
 
 kvq_status check_layer(const kvq_model *m, int32_t layer, const kvq_layer_cache *c)
 {
@@ -125,7 +130,7 @@ kvq_status kvq_pack(const kvq_model *model, int32_t layer, const kvq_layer_cache
     p.batch = cache->batch;
     p.max_tokens = max_tokens;
     p.max_pages = cache->max_pages;
-    return hip_status(kvq::launch_pack(model->k_bits[layer], model->v_bits[layer], p,
+    return hip_status(kvq::launch_pack(model->k_bits[layer], model->v_bits[layer], key_mode(model, layer), p,
                                        src_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
 }
 
@@ -148,7 +153,7 @@ kvq_status kvq_append(const kvq_model *model, int32_t layer, const kvq_layer_cac
     p.H = model->n_kv_heads;
     p.batch = cache->batch;
     p.max_pages = cache->max_pages;
-    return hip_status(kvq::launch_append(model->k_bits[layer], model->v_bits[layer], p,
+    return hip_status(kvq::launch_append(model->k_bits[layer], model->v_bits[layer], key_mode(model, layer), p,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -212,7 +217,7 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     p.max_seq_len = max_seq_len;
     p.pages_per_split = pps;
     p.n_splits = n_splits;
-    return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], p,
+    return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], key_mode(model, layer), p,
                                          q_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
 }
 

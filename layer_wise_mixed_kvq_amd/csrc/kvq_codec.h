@@ -9,9 +9,12 @@
 //   [KVTuner OpenReview discussion (paperhub.cn/paper/zDwipF6h06), reply to reviewer 1,
 //    section 4; reply to reviewer 2, section 2]
 //
-//   1. threads 0..127 each reduce one key channel over the 32 tokens, threads 128..255
-//      each reduce one (token, 32-channel group) of the values -- every thread owns exactly
-//      one group, so the min/max needs no cross-thread reduction;
+// Keys are per channel by default; in the per-token key mode they are grouped like the
+// values (one group per token and 32 consecutive channels).
+//   1. threads 0..127 each reduce one key group (a channel over the 32 tokens, or in the
+//      per-token mode one (token, 32-channel group)), threads 128..255 each reduce one
+//      (token, 32-channel group) of the values -- every thread owns exactly one group, so
+//      the min/max needs no cross-thread reduction;
 //   2. each thread encodes its own 32 values (binary32 subtract and correctly rounded
 //      divide, round half to even, clamp) and writes the codes as bytes to LDS;
 //   3. all 256 threads pack the code bytes into the bit layout and store whole dwords.
@@ -73,20 +76,39 @@ __device__ __forceinline__ void quant_group(float *x, int stride, uint32_t &sz_w
     sz_word = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
 }
 
+// Channel held by slot `slot` of chunk `a` (4*KB bytes) of a token row in the per-token
+// key mode: each chunk holds channels 32J + 8a .. 32J + 8a + 7 of every key group J, the
+// pair 32J + 8a + 2i, + 1 at the same position of the two 16-bit halves of one word --
+// the order in which the decode kernel's matrix-core operands consume them.
+template <int KB>
+__device__ __forceinline__ int ktok_slot_channel(int a, int slot)
+{
+    constexpr int n = 16 / KB;
+    const int x = slot / (2 * n), hh = (slot / n) % 2, p = slot % n;
+    const int k = x * n + p;
+    return 32 * (k / 4) + 8 * a + 2 * (k % 4) + hh;
+}
+
 // Quantize the staged tiles of one page-head into `dst` (global).  All 256 threads of the
 // workgroup call it; with DEQUANT the tiles hold the dequantized values afterwards (valid
-// after the workgroup's next barrier).
-template <int KB, int VB, bool DEQUANT = false>
+// after the workgroup's next barrier).  KTOK selects the per-token key mode.
+template <int KB, int VB, bool DEQUANT = false, bool KTOK = false>
 __device__ void quantize_page(QuantSmem &sm, uint8_t *__restrict__ dst)
 {
     using P = PageLayout<KB, VB>;
     const int tid = threadIdx.x;
     uint32_t *dst32 = reinterpret_cast<uint32_t *>(dst);
     if (tid < kHeadDim) {
-        const int c = tid;
         uint32_t w;
-        quant_group<KB, DEQUANT>(&sm.k[c], kTileStride, w, &sm.kcode[c], kHeadDim);
-        dst32[P::kKSz / 4 + c] = w;
+        if constexpr (KTOK) {
+            const int t = tid & (kGroup - 1), j = tid >> 5;
+            quant_group<KB, DEQUANT>(&sm.k[t * kTileStride + kGroup * j], 1, w, &sm.kcode[t * kHeadDim + kGroup * j], 1);
+            dst32[P::kKSz / 4 + kValueGroups * t + j] = w;
+        } else {
+            const int c = tid;
+            quant_group<KB, DEQUANT>(&sm.k[c], kTileStride, w, &sm.kcode[c], kHeadDim);
+            dst32[P::kKSz / 4 + c] = w;
+        }
     } else {
         const int t = (tid - kHeadDim) & (kGroup - 1);
         const int j = (tid - kHeadDim) >> 5;
@@ -96,14 +118,21 @@ __device__ void quantize_page(QuantSmem &sm, uint8_t *__restrict__ dst)
         dst32[P::kVSz / 4 + kValueGroups * t + j] = w;
     }
     __syncthreads();
-    // K codes: dword d of the section holds 32/KB consecutive channels of one token row
+    // K codes: dword d of the section holds 32/KB slots of one token row (consecutive
+    // channels, or in the per-token mode the channels of ktok_slot_channel)
     constexpr int kPerWord = 32 / KB;
     for (int d = tid; d < 128 * KB; d += kCodecThreads) {
-        const int t = d / (4 * KB);
-        const int c0 = (d % (4 * KB)) * kPerWord;
+        const int t = d / (4 * KB), dr = d % (4 * KB);
         uint32_t w = 0;
 #pragma unroll
-        for (int i = 0; i < kPerWord; ++i) w |= static_cast<uint32_t>(sm.kcode[t * kHeadDim + c0 + i]) << (i * KB);
+        for (int i = 0; i < kPerWord; ++i) {
+            int c;
+            if constexpr (KTOK)
+                c = ktok_slot_channel<KB>(dr / KB, (dr % KB) * kPerWord + i);
+            else
+                c = dr * kPerWord + i;
+            w |= static_cast<uint32_t>(sm.kcode[t * kHeadDim + c]) << (i * KB);
+        }
         dst32[P::kKCodes / 4 + d] = w;
     }
     // V codes: 64 chunks of 2*VB words; chunk 16q + r holds tokens 8q..8q+7 of channels

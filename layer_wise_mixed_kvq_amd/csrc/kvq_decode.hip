@@ -48,7 +48,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxGS = 4;                     // head slots per lane group: G <= 16
+[[maybe_unused]] constexpr int kMaxGS = 4;                   // head slots per lane group: G <= 16
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kScoreScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e)/sqrt(128)
 
@@ -309,7 +309,7 @@ __device__ __forceinline__ void load_residual(const DecodeParams &p, long long b
 // completes a group (flush) the 32 rows are quantized into their page `flush_page` (same
 // codec and bytes as kvq_append) and the tile is replaced by its dequantized values, which
 // are then attended.  Returns false if the flush page id is outside the pool.
-template <int KB, int VB, int GS>
+template <int KB, int VB, int GS, bool KT>
 __device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nres, int G,
                                 long long bh, bool append, bool flush, int flush_page)
 {
@@ -341,7 +341,7 @@ __device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, const
         if (ok) {
             uint8_t *dst = static_cast<uint8_t *>(p.pages) +
                            (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
-            quantize_page<KB, VB, true>(R.q, dst);
+            quantize_page<KB, VB, true, KT>(R.q, dst);
         }
         __syncthreads();
     }
@@ -393,11 +393,12 @@ struct PageRegs {
     uint32_t kc[2][KB];      // key codes of tokens 16*blk + (lane % 16), k-group lane / 16
     uint32_t vc[2 * VB];     // value code chunk `lane`
     uint32_t kszw[2];        // key (s, z) of the two channels this lane folds into q
-    uint32_t kszb[8];        // key (s, z) of channels 8*(lane%16) .. +7 (zero terms, page max)
+    uint32_t kszb[8];        // key (s, z) of channels 8*(lane%16) .. +7 (zero terms, page max);
+                             // per-token keys: (s, z) of groups 0..3 of tokens r16, 16 + r16
     uint32_t vszw[2];        // value (s, z) of the two tokens this lane folds into p
 };
 
-template <int KB, int VB>
+template <int KB, int VB, bool KT>
 __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *base, int lane, int ch0, int ch1,
                                           int t0, int t1)
 {
@@ -424,10 +425,12 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
         r.vc[i] = x.x; r.vc[i + 1] = x.y; r.vc[i + 2] = x.z; r.vc[i + 3] = x.w;
     }
     const uint32_t *ksz = reinterpret_cast<const uint32_t *>(base + PL::kKSz);
-    r.kszw[0] = ksz[ch0];
-    r.kszw[1] = ksz[ch1];
-    const uint4 b0 = *reinterpret_cast<const uint4 *>(ksz + 8 * r16);
-    const uint4 b1 = *reinterpret_cast<const uint4 *>(ksz + 8 * r16 + 4);
+    if constexpr (!KT) {
+        r.kszw[0] = ksz[ch0];
+        r.kszw[1] = ksz[ch1];
+    }
+    const uint4 b0 = *reinterpret_cast<const uint4 *>(ksz + (KT ? kValueGroups * r16 : 8 * r16));
+    const uint4 b1 = *reinterpret_cast<const uint4 *>(ksz + (KT ? kValueGroups * (16 + r16) : 8 * r16 + 4));
     r.kszb[0] = b0.x; r.kszb[1] = b0.y; r.kszb[2] = b0.z; r.kszb[3] = b0.w;
     r.kszb[4] = b1.x; r.kszb[5] = b1.y; r.kszb[6] = b1.z; r.kszb[7] = b1.w;
     const uint32_t *vsz = reinterpret_cast<const uint32_t *>(base + PL::kVSz);
@@ -435,7 +438,8 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
     r.vszw[1] = vsz[kValueGroups * t1 + a];
 }
 
-template <int KB, int VB, int GS, typename QT>
+// KT: per-token keys (one key group per token and 32 channels) instead of per-channel keys
+template <int KB, int VB, int GS, typename QT, bool KT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 {
     using PL = PageLayout<KB, VB>;
@@ -494,8 +498,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     // lane roles in the page loop
     const int a = lane >> 4, r16 = lane & 15;
     const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
-    const int ch0 = 32 * kq + key_pair_channel<KB>(kjj, kj);
-    const int ch1 = ch0 + 16 / KB;
+    // per-channel keys: any channel pair of the lane's 32-channel group; per-token keys: the
+    // pair 32*kjj + 8*kq + 2*kj, + 1, so that matrix-core block kjj is exactly key group kjj
+    const int ch0 = KT ? 32 * kjj + 8 * kq + 2 * kj : 32 * kq + key_pair_channel<KB>(kjj, kj);
+    const int ch1 = KT ? ch0 + 1 : ch0 + 16 / KB;
     const int t0 = 8 * (r16 >> 2) + (r16 & 3), t1 = t0 + 4;   // value pair this lane folds (group a)
     // powers of two the code unpack leaves on this lane's key channels / value tokens
     const int kshift = unpack_shift<KB>(kj), vshift = unpack_shift<VB>(r16 & 3);
@@ -509,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         return pool + (static_cast<long long>(phys) * p.H + h) * PL::kBytes;
     };
     PageRegs<KB, VB> cur, nxt;
-    if (n_my > 0) load_page<KB, VB>(cur, page_base(0), lane, ch0, ch1, t0, t1);
+    if (n_my > 0) load_page<KB, VB, KT>(cur, page_base(0), lane, ch0, ch1, t0, t1);
 #pragma unroll
     for (int k = 0; k < kQPer; ++k) {
         const int i = tid + k * kThreads;
@@ -555,6 +561,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             for (int x = 0; x < 8; ++x) qb[i][x] = hh < G ? ldexpf(sm.qs[hh][8 * r16 + x], sm.eq[hh]) : 0.0f;
             inv_eq[i] = hh < G ? ldexpf(1.0f, -sm.eq[hh]) : 0.0f;
         }
+        // per-token keys: the A operand is q~ itself (page-invariant), folded once; the zero
+        // terms need q~ summed over each key group: qsum[i][J] for head 4i + a
+        float qsum[GS][4];
+        if constexpr (KT) {
+            const float f = ldexpf(1.0f, -kshift);
+#pragma unroll
+            for (int hh = 0; hh < HS; ++hh) {
+                const uint32_t hi = split_hi(qw[hh][0] * f, qw[hh][1] * f);
+                W.qp[0][hh][lane] = hi;
+                W.qp[1][hh][lane] = split_lo(qw[hh][0], f, qw[hh][1], f, hi);
+            }
+#pragma unroll
+            for (int i = 0; i < GS; ++i) {
+                const int hh = 4 * i + a;
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    const float x = hh < G ? ldexpf(sm.qs[hh][32 * J + 2 * r16] + sm.qs[hh][32 * J + 2 * r16 + 1],
+                                                    sm.eq[hh])
+                                           : 0.0f;
+                    qsum[i][J] = row_sum(x);
+                }
+            }
+            wave_lds_sync();
+        }
 
         const uint32_t magic = fp16x2_1024();
         float4_t acc[8];
@@ -575,6 +605,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         int ev = 127;
 
         auto process_page = [&](const PageRegs<KB, VB> &cur) {
+          float s2[2][GS];
+          if constexpr (!KT) {
             // ---- page exponent: |q~ s 2^E| < 2^15 for every channel ---------------
             uint32_t smax = 0;
 #pragma unroll
@@ -620,19 +652,48 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     sacc[blk] = mfma(alo, bk, sacc[blk]);
                 }
             }
-            // ---- online softmax ------------------------------------------------------
-            float s2[2][GS];
-            bool grow = false;
             const float sce = ldexpf(1.0f, -E);
 #pragma unroll
             for (int i = 0; i < GS; ++i) {
                 const float sc = sce * inv_eq[i];
                 const float bc = bias[i] * inv_eq[i];
 #pragma unroll
+                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = fmaf(sacc[blk][i], sc, bc);
+            }
+          } else {
+            // ---- per-token keys: one accumulator per key group, then the token's scales --
+            float4_t sk[4][2];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const uint4 ahi = lds_read16(&W.qp[0][arow][16 * a + 4 * jj]);
+                const uint4 alo = lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
+#pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
-                    s2[blk][i] = fmaf(sacc[blk][i], sc, bc);
-                    grow |= (4 * i + a < G) && s2[blk][i] > m_run[i];
+                    const uint4 bk = unpack_codes<KB>(cur.kc[blk], jj, magic);
+                    sk[jj][blk] = mfma(alo, bk, mfma(ahi, bk, float4_t{0.f, 0.f, 0.f, 0.f}));
                 }
+            }
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+                for (int i = 0; i < GS; ++i) {
+                    float raw = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const uint32_t w = cur.kszb[4 * blk + jj];
+                        raw = fmaf(half_bits_to_float(w & 0xFFFFu), sk[jj][blk][i], raw);
+                        raw = fmaf(half_bits_to_float(w >> 16), qsum[i][jj], raw);
+                    }
+                    s2[blk][i] = raw * inv_eq[i];
+                }
+            }
+          }
+            // ---- online softmax ------------------------------------------------------
+            bool grow = false;
+#pragma unroll
+            for (int i = 0; i < GS; ++i) {
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) grow |= (4 * i + a < G) && s2[blk][i] > m_run[i];
             }
             if (__any(grow)) {
                 float alpha[GS];
@@ -711,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         // an L2 hit), so the compiler's wait counts see one path and wait only for the page
         // about to be used, never for the one just requested.
         auto prefetch = [&](PageRegs<KB, VB> &dst, int j) {
-            load_page<KB, VB>(dst, page_base(min(j, n_my - 1)), lane, ch0, ch1, t0, t1);
+            load_page<KB, VB, KT>(dst, page_base(min(j, n_my - 1)), lane, ch0, ch1, t0, t1);
         };
         int j = 0;
         for (; j + 1 < n_my; j += 2) {
@@ -739,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(acc[nb][i], unscale, W.bv[nb >> 1][4 * i + a]);
         __syncthreads();     // every wave is done with its WaveLds: reuse the space
-        if (has_res) bad_page |= !residual_tokens<KB, VB, GS>(p, sm, res_kv, nres, G, bh, append, flush, full);
+        if (has_res) bad_page |= !residual_tokens<KB, VB, GS, KT>(p, sm, res_kv, nres, G, bh, append, flush, full);
         MergeLds<GS> &M = sm.u.merge;
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
@@ -754,7 +815,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             }
         }
     } else if (has_res) {
-        bad_page |= !residual_tokens<KB, VB, GS>(p, sm, res_kv, nres, G, bh, append, flush, full);
+        bad_page |= !residual_tokens<KB, VB, GS, KT>(p, sm, res_kv, nres, G, bh, append, flush, full);
     }
 
     // ---- this workgroup's merge: its waves' page states and, on the last split, the residual
@@ -900,36 +961,60 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     if (tid == 0) __hip_atomic_store(p.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+#if defined(KVQ_DECODE_COMMON)
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words)
 {
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words;
          i += static_cast<size_t>(gridDim.x) * blockDim.x)
         p[i] = 0u;
 }
+#endif
 
-template <int KB, int VB, int GS>
+template <int KB, int VB, int GS, bool KT>
 hipError_t launch_decode_g(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
     dim3 grid(p.H, p.batch, p.n_splits);
     if (q_f32)
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float, KT>), grid, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t, KT>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <int KB, int VB>
-hipError_t launch_decode_t(const DecodeParams &p, bool q_f32, hipStream_t s)
+template <int KB, int VB, bool KT>
+hipError_t launch_decode_k(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
-    if (p.G <= 4) return launch_decode_g<KB, VB, 1>(p, q_f32, s);
-    if (p.G <= 8) return launch_decode_g<KB, VB, 2>(p, q_f32, s);
-    return launch_decode_g<KB, VB, 4>(p, q_f32, s);
+    if (p.G <= 4) return launch_decode_g<KB, VB, 1, KT>(p, q_f32, s);
+    if (p.G <= 8) return launch_decode_g<KB, VB, 2, KT>(p, q_f32, s);
+    return launch_decode_g<KB, VB, 4, KT>(p, q_f32, s);
+}
+
+template <int KB, int VB>
+hipError_t launch_decode_t(int kmode, const DecodeParams &p, bool q_f32, hipStream_t s)
+{
+    return kmode ? launch_decode_k<KB, VB, true>(p, q_f32, s) : launch_decode_k<KB, VB, false>(p, q_f32, s);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
+// This source is compiled once per key bit width (KVQ_DECODE_KB = 2, 4, 8: the kernels of
+// that width) and once with KVQ_DECODE_COMMON (host helpers and the dispatch), so that the
+// kernel instantiations build in parallel.
+#if defined(KVQ_DECODE_KB)
+#define KVQ_LAUNCH_KB_NAME_(KBV) launch_decode_kb##KBV
+#define KVQ_LAUNCH_KB_NAME(KBV) KVQ_LAUNCH_KB_NAME_(KBV)
+hipError_t KVQ_LAUNCH_KB_NAME(KVQ_DECODE_KB)(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s)
+{
+    if (vb == 2) return launch_decode_t<KVQ_DECODE_KB, 2>(kmode, p, q_f32, s);
+    if (vb == 4) return launch_decode_t<KVQ_DECODE_KB, 4>(kmode, p, q_f32, s);
+    if (vb == 8) return launch_decode_t<KVQ_DECODE_KB, 8>(kmode, p, q_f32, s);
+    return hipErrorInvalidValue;
+}
+#endif
+
+#if defined(KVQ_DECODE_COMMON)
 DecodeWorkspace decode_workspace_layout(int batch, int H, int G, int n_splits)
 {
     DecodeWorkspace w;
@@ -956,13 +1041,11 @@ int decode_default_pages_per_split(int batch, int H, int max_full_pages)
 
 int decode_max_g() { return 4 * kMaxGS; }
 
-hipError_t launch_decode(int kb, int vb, const DecodeParams &p, bool q_f32, hipStream_t s)
+hipError_t launch_decode(int kb, int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s)
 {
-#define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_decode_t<KBV, VBV>(p, q_f32, s)
-    KVQ_P(2, 2); KVQ_P(2, 4); KVQ_P(2, 8);
-    KVQ_P(4, 2); KVQ_P(4, 4); KVQ_P(4, 8);
-    KVQ_P(8, 2); KVQ_P(8, 4); KVQ_P(8, 8);
-#undef KVQ_P
+    if (kb == 2) return launch_decode_kb2(vb, kmode, p, q_f32, s);
+    if (kb == 4) return launch_decode_kb4(vb, kmode, p, q_f32, s);
+    if (kb == 8) return launch_decode_kb8(vb, kmode, p, q_f32, s);
     return hipErrorInvalidValue;
 }
 
@@ -976,5 +1059,6 @@ hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t s)
                        static_cast<uint32_t *>(ptr), words);
     return hipGetLastError();
 }
+#endif  // KVQ_DECODE_COMMON
 
 }  // namespace kvq

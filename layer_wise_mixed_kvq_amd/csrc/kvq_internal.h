@@ -67,9 +67,14 @@ struct DecodeWorkspace {
 DecodeWorkspace decode_workspace_layout(int batch, int H, int G, int n_splits);
 int decode_default_pages_per_split(int batch, int H, int max_full_pages);
 
-hipError_t launch_pack(int kb, int vb, const PackParams &p, bool src_f32, hipStream_t s);
-hipError_t launch_append(int kb, int vb, const AppendParams &p, hipStream_t s);
-hipError_t launch_decode(int kb, int vb, const DecodeParams &p, bool q_f32, hipStream_t s);
+// kmode: 0 = per-channel keys, 1 = per-token keys
+hipError_t launch_pack(int kb, int vb, int kmode, const PackParams &p, bool src_f32, hipStream_t s);
+hipError_t launch_append(int kb, int vb, int kmode, const AppendParams &p, hipStream_t s);
+hipError_t launch_decode(int kb, int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
+// the kernels of one key bit width (each built in its own translation unit)
+hipError_t launch_decode_kb2(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
+hipError_t launch_decode_kb4(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
+hipError_t launch_decode_kb8(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t s);
 
 }  // namespace kvq

@@ -67,7 +67,7 @@ __device__ void stage_tile(const SrcT *__restrict__ src, long long row_stride, f
 }
 
 // grid: (pages covering max_tokens, n_kv_heads, batch)
-template <int KB, int VB, typename SrcT>
+template <int KB, int VB, bool KTOK, typename SrcT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 {
     __shared__ QuantSmem sm;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
         __syncthreads();
         uint8_t *dst = static_cast<uint8_t *>(p.pages) +
                        (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
-        quantize_page<KB, VB>(sm, dst);
+        quantize_page<KB, VB, false, KTOK>(sm, dst);
     } else if (g == full) {
         // trailing L mod 32 tokens -> bf16 residual slots 0 .. L mod 32 - 1
         const int nres = L - full * kGroup;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 }
 
 // grid: (n_kv_heads, batch)
-template <int KB, int VB>
+template <int KB, int VB, bool KTOK>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p)
 {
     __shared__ QuantSmem sm;
@@ -133,37 +133,43 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p)
     }
     __syncthreads();
     uint8_t *dst = static_cast<uint8_t *>(p.pages) + (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
-    quantize_page<KB, VB>(sm, dst);
+    quantize_page<KB, VB, false, KTOK>(sm, dst);
 }
 
-template <int KB, int VB>
-hipError_t launch_pack_t(const PackParams &p, bool src_f32, hipStream_t s)
+template <int KB, int VB, bool KTOK>
+hipError_t launch_pack_m(const PackParams &p, bool src_f32, hipStream_t s)
 {
     const int gx = (p.max_tokens + kGroup - 1) / kGroup;
     if (gx == 0) return hipSuccess;
     dim3 grid(gx, p.H, p.batch);
     if (src_f32)
-        hipLaunchKernelGGL((pack_kernel<KB, VB, float>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((pack_kernel<KB, VB, KTOK, float>), grid, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((pack_kernel<KB, VB, uint16_t>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((pack_kernel<KB, VB, KTOK, uint16_t>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 template <int KB, int VB>
-hipError_t launch_append_t(const AppendParams &p, hipStream_t s)
+hipError_t launch_pack_t(int kmode, const PackParams &p, bool src_f32, hipStream_t s)
 {
-    hipLaunchKernelGGL((append_kernel<KB, VB>), dim3(p.H, p.batch), dim3(kThreads), 0, s, p);
+    return kmode ? launch_pack_m<KB, VB, true>(p, src_f32, s) : launch_pack_m<KB, VB, false>(p, src_f32, s);
+}
+
+template <int KB, int VB>
+hipError_t launch_append_t(int kmode, const AppendParams &p, hipStream_t s)
+{
+    if (kmode)
+        hipLaunchKernelGGL((append_kernel<KB, VB, true>), dim3(p.H, p.batch), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((append_kernel<KB, VB, false>), dim3(p.H, p.batch), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#define KVQ_DISPATCH_PAIR(KBV, VBV, CALL) \
-    if (kb == KBV && vb == VBV) return CALL<KBV, VBV>
-
-hipError_t launch_pack(int kb, int vb, const PackParams &p, bool src_f32, hipStream_t s)
+hipError_t launch_pack(int kb, int vb, int kmode, const PackParams &p, bool src_f32, hipStream_t s)
 {
-#define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_pack_t<KBV, VBV>(p, src_f32, s)
+#define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_pack_t<KBV, VBV>(kmode, p, src_f32, s)
     KVQ_P(2, 2); KVQ_P(2, 4); KVQ_P(2, 8);
     KVQ_P(4, 2); KVQ_P(4, 4); KVQ_P(4, 8);
     KVQ_P(8, 2); KVQ_P(8, 4); KVQ_P(8, 8);
@@ -171,9 +177,9 @@ hipError_t launch_pack(int kb, int vb, const PackParams &p, bool src_f32, hipStr
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_append(int kb, int vb, const AppendParams &p, hipStream_t s)
+hipError_t launch_append(int kb, int vb, int kmode, const AppendParams &p, hipStream_t s)
 {
-#define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_append_t<KBV, VBV>(p, s)
+#define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_append_t<KBV, VBV>(kmode, p, s)
     KVQ_P(2, 2); KVQ_P(2, 4); KVQ_P(2, 8);
     KVQ_P(4, 2); KVQ_P(4, 4); KVQ_P(4, 8);
     KVQ_P(8, 2); KVQ_P(8, 4); KVQ_P(8, 8);

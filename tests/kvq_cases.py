@@ -33,9 +33,10 @@ class Case:
     """One layer's seeded inputs plus its oracle cache and its device cache."""
 
     def __init__(self, kb, vb, H, G, lens, *, seed=1, layer=0, src="bf16", q_dtype="bf16", shuffle=True,
-                 extra_pages=3, n_outliers=3, spare_pages_per_seq=0):
+                 extra_pages=3, n_outliers=3, spare_pages_per_seq=0, kmode=0):
         import torch
         self.kb, self.vb, self.H, self.G = kb, vb, H, G
+        self.kmode = kmode            # 0: per-channel keys, 1: per-token keys
         self.lens = np.array(lens, dtype=np.int32)
         self.B = len(lens)
         self.T = max(1, int(self.lens.max()))
@@ -54,17 +55,17 @@ class Case:
     def oracle_pack(self, orc):
         self.o_pages, self.o_rk, self.o_rv = orc.new_cache(self.kb, self.vb, self.H, self.B, self.n_phys)
         orc.pack(self.kb, self.vb, host_array(self.k), host_array(self.v), self.lens, self.bt,
-                 self.o_pages, self.o_rk, self.o_rv)
+                 self.o_pages, self.o_rk, self.o_rv, kmode=self.kmode)
 
     def oracle_decode(self, orc, lens=None):
         lens = self.lens if lens is None else np.asarray(lens, dtype=np.int32)
         return orc.decode_attn(self.kb, self.vb, self.H, host_array(self.q), lens, self.bt, self.o_pages,
-                               self.o_rk, self.o_rv)
+                               self.o_rk, self.o_rv, kmode=self.kmode)
 
     # ---- device side -------------------------------------------------------------
     def device_setup(self, kvq):
         import torch
-        self.model = kvq.Model([(self.kb, self.vb)], self.H * self.G, self.H)
+        self.model = kvq.Model([(self.kb, self.vb, self.kmode)], self.H * self.G, self.H)
         self.bt_d = torch.from_numpy(self.bt).to(self.dev)
         self.cache = kvq.LayerCache(self.model, 0, self.B, self.maxp, n_pages=self.n_phys,
                                     block_table=self.bt_d, device=self.dev)

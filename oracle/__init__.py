@@ -70,6 +70,23 @@ def lib() -> ctypes.CDLL:
         L.orc_quant_group.restype = ci
         L.orc_head_page_bytes.argtypes = [ci, ci]
         L.orc_head_page_bytes.restype = ctypes.c_size_t
+        L.orc_fp8_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_fp8_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_fp8.argtypes = [ctypes.c_float]
+        L.orc_f32_to_fp8.restype = ctypes.c_uint8
+        L.orc_head_page_bytes_x.argtypes = [ci, ci, ci]
+        L.orc_head_page_bytes_x.restype = ctypes.c_size_t
+        L.orc_pack_page_x.argtypes = [f32p, f32p, ci, ci, ci, ci, ctypes.c_float, ctypes.c_float, u8p]
+        L.orc_pack_page_x.restype = ci
+        L.orc_dequant_page_x.argtypes = [u8p, ci, ci, ci, ctypes.c_float, ctypes.c_float, f64p, f64p]
+        L.orc_dequant_page_x.restype = ci
+        L.orc_pack_x.argtypes = [ci, ci, ci, f32p, ci, ci, ci, ci, vp, vp, i32p, i32p, ci, u8p, u16p, u16p]
+        L.orc_pack_x.restype = ci
+        L.orc_append_x.argtypes = [ci, ci, ci, f32p, ci, ci, u16p, u16p, i32p, i32p, ci, u8p, u16p, u16p]
+        L.orc_append_x.restype = ci
+        L.orc_decode_attn_x.argtypes = [ci, ci, ci, f32p, ci, ci, ci, ci, vp, i32p, i32p, ci, u8p, u16p, u16p,
+                                        f64p, f64p]
+        L.orc_decode_attn_x.restype = ci
         L.orc_pack_page_m.argtypes = [f32p, f32p, ci, ci, ci, ci, u8p]
         L.orc_pack_page_m.restype = ci
         L.orc_dequant_page_m.argtypes = [u8p, ci, ci, ci, f64p, f64p]
@@ -131,27 +148,51 @@ def head_page_bytes(kb: int, vb: int) -> int:
     return int(lib().orc_head_page_bytes(kb, vb))
 
 
-KMODE_CHANNEL, KMODE_TOKEN = 0, 1   # keys per channel over 32 tokens / per token over 32 channels
+# layer formats: integer codes with per-channel keys / per-token keys, OCP FP8 E4M3 with
+# per-head scales (kb = vb = 8), BF16 (kb = vb = 16)
+KMODE_CHANNEL, KMODE_TOKEN, FMT_FP8, FMT_BF16 = 0, 1, 2, 3
 
 
-def pack_page(k_tile: np.ndarray, v_tile: np.ndarray, kb: int, vb: int, kmode: int = KMODE_CHANNEL) -> np.ndarray:
-    """Quantize one 32x128 fp32 K tile and V tile into one packed page (uint8)."""
+def fp8_to_f32(b: int) -> float:
+    return float(lib().orc_fp8_to_f32(b))
+
+
+def f32_to_fp8(x: float) -> int:
+    return int(lib().orc_f32_to_fp8(x))
+
+
+def head_page_bytes_fmt(kb: int, vb: int, fmt: int) -> int:
+    return int(lib().orc_head_page_bytes_x(kb, vb, fmt))
+
+
+def pack_page(k_tile: np.ndarray, v_tile: np.ndarray, kb: int, vb: int, kmode: int = KMODE_CHANNEL,
+              ks: float = 1.0, vs: float = 1.0) -> np.ndarray:
+    """Quantize one 32x128 fp32 K tile and V tile into one packed page (uint8); kmode is
+    the layer format (KMODE_* / FMT_*), ks / vs the FP8 scales."""
     k = np.ascontiguousarray(k_tile, dtype=np.float32).reshape(GROUP, HEAD_DIM)
     v = np.ascontiguousarray(v_tile, dtype=np.float32).reshape(GROUP, HEAD_DIM)
-    out = np.zeros(head_page_bytes(kb, vb), dtype=np.uint8)
-    _check(lib().orc_pack_page_m(_ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), HEAD_DIM, kb, vb, kmode,
-                                 _ptr(out, ctypes.c_uint8)), "pack_page")
+    out = np.zeros(head_page_bytes_fmt(kb, vb, kmode), dtype=np.uint8)
+    _check(lib().orc_pack_page_x(_ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), HEAD_DIM, kb, vb, kmode,
+                                 ks, vs, _ptr(out, ctypes.c_uint8)), "pack_page")
     return out
 
 
-def dequant_page(page: np.ndarray, kb: int, vb: int, kmode: int = KMODE_CHANNEL):
+def dequant_page(page: np.ndarray, kb: int, vb: int, kmode: int = KMODE_CHANNEL, ks: float = 1.0,
+                 vs: float = 1.0):
     """Packed page -> (K, V) float64 [32][128]."""
     p = np.ascontiguousarray(page, dtype=np.uint8)
     k = np.zeros((GROUP, HEAD_DIM), dtype=np.float64)
     v = np.zeros((GROUP, HEAD_DIM), dtype=np.float64)
-    _check(lib().orc_dequant_page_m(_ptr(p, ctypes.c_uint8), kb, vb, kmode, _ptr(k, ctypes.c_double),
+    _check(lib().orc_dequant_page_x(_ptr(p, ctypes.c_uint8), kb, vb, kmode, ks, vs, _ptr(k, ctypes.c_double),
                                     _ptr(v, ctypes.c_double)), "dequant_page")
     return k, v
+
+
+def _scales_ptr(scales, H):
+    if scales is None:
+        return None, None
+    a = np.ascontiguousarray(scales, dtype=np.float32).reshape(H, 2)
+    return a, _ptr(a, ctypes.c_float)
 
 
 # --------------------------------------------------------------------------------------
@@ -169,8 +210,10 @@ def _src_kind(a: np.ndarray) -> int:
 
 
 def pack(kb: int, vb: int, k_src: np.ndarray, v_src: np.ndarray, seq_len, block_table,
-         pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL) -> None:
-    """Prefill quantize-on-write; k_src, v_src are [B][T][H][128]; updates in place."""
+         pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL,
+         scales=None) -> None:
+    """Prefill quantize-on-write; k_src, v_src are [B][T][H][128]; updates in place.
+    kmode is the layer format; scales (FP8) is [H][2] (K, V), None for all 1."""
     B, T, H, D = k_src.shape
     assert D == HEAD_DIM and v_src.shape == k_src.shape and v_src.dtype == k_src.dtype
     kind = _src_kind(k_src)
@@ -178,14 +221,16 @@ def pack(kb: int, vb: int, k_src: np.ndarray, v_src: np.ndarray, seq_len, block_
     v_src = np.ascontiguousarray(v_src)
     sl = np.ascontiguousarray(seq_len, dtype=np.int32)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
-    _check(lib().orc_pack_m(kb, vb, kmode, H, B, T, kind, k_src.ctypes.data, v_src.ctypes.data,
+    keep, sp = _scales_ptr(scales, H)
+    _check(lib().orc_pack_x(kb, vb, kmode, sp, H, B, T, kind, k_src.ctypes.data, v_src.ctypes.data,
                           _ptr(sl, ctypes.c_int32), _ptr(bt, ctypes.c_int32), bt.shape[1],
                           _ptr(pages, ctypes.c_uint8), _ptr(resid_k, ctypes.c_uint16),
                           _ptr(resid_v, ctypes.c_uint16)), "pack")
 
 
 def append(kb: int, vb: int, k_new: np.ndarray, v_new: np.ndarray, pos, block_table,
-           pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL) -> None:
+           pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL,
+           scales=None) -> None:
     """Decode-time write of one bf16 token per sequence ([B][H][128] uint16); in place."""
     B, H, D = k_new.shape
     assert D == HEAD_DIM and k_new.dtype == np.uint16 and v_new.dtype == np.uint16
@@ -193,14 +238,16 @@ def append(kb: int, vb: int, k_new: np.ndarray, v_new: np.ndarray, pos, block_ta
     vn = np.ascontiguousarray(v_new)
     p = np.ascontiguousarray(pos, dtype=np.int32)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
-    _check(lib().orc_append_m(kb, vb, kmode, H, B, _ptr(kn, ctypes.c_uint16), _ptr(vn, ctypes.c_uint16),
+    keep, sp = _scales_ptr(scales, H)
+    _check(lib().orc_append_x(kb, vb, kmode, sp, H, B, _ptr(kn, ctypes.c_uint16), _ptr(vn, ctypes.c_uint16),
                             _ptr(p, ctypes.c_int32), _ptr(bt, ctypes.c_int32), bt.shape[1],
                             _ptr(pages, ctypes.c_uint8), _ptr(resid_k, ctypes.c_uint16),
                             _ptr(resid_v, ctypes.c_uint16)), "append")
 
 
 def decode_attn(kb: int, vb: int, n_kv_heads: int, q: np.ndarray, seq_len, block_table,
-                pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL):
+                pages: np.ndarray, resid_k: np.ndarray, resid_v: np.ndarray, kmode: int = KMODE_CHANNEL,
+                scales=None):
     """binary64 decode attention; q is [B][Hq][128] (bf16 bits as uint16, or float32).
     Returns (out float64 [B][Hq][128], lse float64 [B][Hq])."""
     B, Hq, D = q.shape
@@ -211,7 +258,8 @@ def decode_attn(kb: int, vb: int, n_kv_heads: int, q: np.ndarray, seq_len, block
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     out = np.zeros((B, Hq, D), dtype=np.float64)
     lse = np.zeros((B, Hq), dtype=np.float64)
-    _check(lib().orc_decode_attn_m(kb, vb, kmode, Hq, n_kv_heads, B, kind, q.ctypes.data,
+    keep, sp = _scales_ptr(scales, n_kv_heads)
+    _check(lib().orc_decode_attn_x(kb, vb, kmode, sp, Hq, n_kv_heads, B, kind, q.ctypes.data,
                                  _ptr(sl, ctypes.c_int32), _ptr(bt, ctypes.c_int32), bt.shape[1],
                                  _ptr(pages, ctypes.c_uint8), _ptr(resid_k, ctypes.c_uint16),
                                  _ptr(resid_v, ctypes.c_uint16), _ptr(out, ctypes.c_double),
@@ -219,9 +267,9 @@ def decode_attn(kb: int, vb: int, n_kv_heads: int, q: np.ndarray, seq_len, block
     return out, lse
 
 
-def new_cache(kb: int, vb: int, n_kv_heads: int, batch: int, n_phys_pages: int):
+def new_cache(kb: int, vb: int, n_kv_heads: int, batch: int, n_phys_pages: int, fmt: int = KMODE_CHANNEL):
     """Zeroed host cache: (pages [P][H][page bytes], resid_k, resid_v [B][H][32][128])."""
-    pages = np.zeros((n_phys_pages, n_kv_heads, head_page_bytes(kb, vb)), dtype=np.uint8)
+    pages = np.zeros((n_phys_pages, n_kv_heads, head_page_bytes_fmt(kb, vb, fmt)), dtype=np.uint8)
     rk = np.zeros((batch, n_kv_heads, GROUP, HEAD_DIM), dtype=np.uint16)
     rv = np.zeros((batch, n_kv_heads, GROUP, HEAD_DIM), dtype=np.uint16)
     return pages, rk, rv

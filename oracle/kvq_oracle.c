@@ -123,6 +123,45 @@ uint16_t orc_f32_to_bf16(float xf)
     return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)(n - 128.0));
 }
 
+/* OCP FP8 E4M3 (the "fn" variant): 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits;
+ * no infinities, S.1111.111 is NaN, the largest finite value is 448 = 1.75 * 2^8.
+ * Normal (e >= 1): (8 + m) * 2^(e - 10); subnormal (e == 0): m * 2^-9. */
+float orc_fp8_to_f32(uint8_t b)
+{
+    int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return (float)(sign ? -v : v);
+}
+
+/* Round a binary32 value to the nearest E4M3 value, ties to even; finite values beyond
+ * the largest finite E4M3 value saturate to +-448 (the format has no infinity). */
+uint8_t orc_f32_to_fp8(float xf)
+{
+    double x = xf;
+    uint8_t sign = signbit(x) ? 0x80u : 0u;
+    if (isnan(x)) return (uint8_t)(sign | 0x7fu);
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint8_t)(sign | 0x7eu);
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;
+    if (E < -6) E = -6;          /* subnormals share the spacing of the lowest normal binade */
+    double quantum = ldexp(1.0, E - 3);
+    double n = nearbyint(a / quantum);
+    if (n == 0.0) return sign;
+    if (n >= 16.0) { n /= 2.0; E += 1; }
+    if (E > 8 || (E == 8 && n > 14.0)) return (uint8_t)(sign | 0x7eu);   /* saturate to 448 */
+    if (n < 8.0) return (uint8_t)(sign | (uint8_t)n);
+    return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)(n - 8.0));
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* the group codec                                                                      */
 /* ------------------------------------------------------------------------------------ */
@@ -319,6 +358,93 @@ int orc_pack_page(const float *k, const float *v, int tok_stride, int kb, int vb
     return orc_pack_page_m(k, v, tok_stride, kb, vb, KMODE_CHANNEL, dst);
 }
 
+/* Floating-point layer formats (a layer stores its K and V in one of them instead of the
+ * integer codes): FMT_FP8 keeps x / scale as OCP E4M3 with one K scale and one V scale per
+ * (layer, KV head); FMT_BF16 keeps x as bfloat16.  [When should you use mixed-precision
+ * KV caching to preserve accuracy in sensitive transformer layers (machinoai.in),
+ * sections 1-2: sensitive layers in BF16, the rest in FP8, per-head calibration scales]
+ * Head page: K token-major [32][128] elements at +0, then V channel-major [128][32]
+ * (element (t, c) at c*32 + t), 1 byte (FP8) or 2 bytes (BF16) per element.  The division
+ * x / scale is one IEEE binary32 division, then rounding to E4M3. */
+enum { FMT_INT_CHANNEL = 0, FMT_INT_TOKEN = 1, FMT_FP8 = 2, FMT_BF16 = 3 };
+
+int orc_dequant_page_m(const uint8_t *src, int kb, int vb, int kmode, double *k, double *v);
+
+static int valid_format(int kb, int vb, int fmt)
+{
+    if (fmt == FMT_INT_CHANNEL || fmt == FMT_INT_TOKEN) return valid_bits(kb) && valid_bits(vb);
+    if (fmt == FMT_FP8) return kb == 8 && vb == 8;
+    if (fmt == FMT_BF16) return kb == 16 && vb == 16;
+    return 0;
+}
+
+size_t orc_head_page_bytes_x(int kb, int vb, int fmt)
+{
+    if (!valid_format(kb, vb, fmt)) return 0;
+    if (fmt == FMT_FP8) return (size_t)ORC_G * ORC_D * 2;
+    if (fmt == FMT_BF16) return (size_t)ORC_G * ORC_D * 4;
+    return orc_head_page_bytes(kb, vb);
+}
+
+static void pack_page_float(const float *k, const float *v, int tok_stride, int fmt, float ks, float vs,
+                            uint8_t *dst)
+{
+    const size_t esz = fmt == FMT_FP8 ? 1 : 2;
+    uint8_t *vdst = dst + (size_t)ORC_G * ORC_D * esz;
+    for (int t = 0; t < ORC_G; ++t)
+        for (int c = 0; c < ORC_D; ++c) {
+            float kx = k[(size_t)t * tok_stride + c], vx = v[(size_t)t * tok_stride + c];
+            size_t ki = (size_t)t * ORC_D + c, vi = (size_t)c * ORC_G + t;
+            if (fmt == FMT_FP8) {
+                dst[ki] = orc_f32_to_fp8(kx / ks);
+                vdst[vi] = orc_f32_to_fp8(vx / vs);
+            } else {
+                uint16_t kb16 = orc_f32_to_bf16(kx), vb16 = orc_f32_to_bf16(vx);
+                dst[2 * ki] = (uint8_t)kb16; dst[2 * ki + 1] = (uint8_t)(kb16 >> 8);
+                vdst[2 * vi] = (uint8_t)vb16; vdst[2 * vi + 1] = (uint8_t)(vb16 >> 8);
+            }
+        }
+}
+
+/* binary64 values; E4M3 value times a binary32 scale is exact in binary64 */
+static void dequant_page_float(const uint8_t *src, int fmt, float ks, float vs, double *k, double *v)
+{
+    const size_t esz = fmt == FMT_FP8 ? 1 : 2;
+    const uint8_t *vsrc = src + (size_t)ORC_G * ORC_D * esz;
+    for (int t = 0; t < ORC_G; ++t)
+        for (int c = 0; c < ORC_D; ++c) {
+            size_t ki = (size_t)t * ORC_D + c, vi = (size_t)c * ORC_G + t;
+            if (fmt == FMT_FP8) {
+                k[ki] = (double)orc_fp8_to_f32(src[ki]) * (double)ks;
+                v[ki] = (double)orc_fp8_to_f32(vsrc[vi]) * (double)vs;
+            } else {
+                k[ki] = orc_bf16_to_f32((uint16_t)(src[2 * ki] | src[2 * ki + 1] << 8));
+                v[ki] = orc_bf16_to_f32((uint16_t)(vsrc[2 * vi] | vsrc[2 * vi + 1] << 8));
+            }
+        }
+}
+
+int orc_pack_page_x(const float *k, const float *v, int tok_stride, int kb, int vb, int fmt, float ks, float vs,
+                    uint8_t *dst)
+{
+    if (!valid_format(kb, vb, fmt)) return 1;
+    if (fmt == FMT_FP8 || fmt == FMT_BF16) {
+        pack_page_float(k, v, tok_stride, fmt, ks, vs, dst);
+        return 0;
+    }
+    return orc_pack_page_m(k, v, tok_stride, kb, vb, fmt, dst);
+}
+
+int orc_dequant_page_x(const uint8_t *src, int kb, int vb, int fmt, float ks, float vs, double *k, double *v)
+{
+    if (!valid_format(kb, vb, fmt)) return 1;
+    if (fmt == FMT_FP8 || fmt == FMT_BF16) {
+        dequant_page_float(src, fmt, ks, vs, k, v);
+        return 0;
+    }
+    return orc_dequant_page_m(src, kb, vb, fmt, k, v);
+}
+
 /* Decode one page into binary64 K and V tiles [32][128].  code * s + z is exact in
  * binary64 (an 8-bit integer times a binary16 value plus a binary16 value). */
 int orc_dequant_page_m(const uint8_t *src, int kb, int vb, int kmode, double *k, double *v)
@@ -370,13 +496,18 @@ static uint16_t src_to_bf16(const void *src, int is_bf16, size_t i)
  * k_src / v_src [batch][max_tokens][H][128] (bf16 or fp32).  Full 32-token groups go to
  * the pages named by the block table; the last seq_len mod 32 tokens go, as bf16, to
  * residual slot t mod 32 of resid_k / resid_v [batch][H][32][128]. */
-int orc_pack_m(int kb, int vb, int kmode, int H, int batch, int max_tokens, int src_is_bf16,
+/* Layer-level operations take a format code fmt (FMT_*; for the integer formats it is the
+ * key mode) and, for FP8, scales[2*h] / scales[2*h + 1] = K / V scale of KV head h (NULL:
+ * every scale 1). */
+static float scale_of(const float *scales, int h, int which) { return scales ? scales[2 * h + which] : 1.0f; }
+
+int orc_pack_x(int kb, int vb, int fmt, const float *scales, int H, int batch, int max_tokens, int src_is_bf16,
                const void *k_src, const void *v_src, const int32_t *seq_len,
                const int32_t *block_table, int max_pages,
                uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
 {
-    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
-    const size_t hp = orc_head_page_bytes(kb, vb);
+    if (!valid_format(kb, vb, fmt)) return 1;
+    const size_t hp = orc_head_page_bytes_x(kb, vb, fmt);
     static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
     for (int b = 0; b < batch; ++b) {
         int L = seq_len[b];
@@ -391,7 +522,8 @@ int orc_pack_m(int kb, int vb, int kmode, int H, int batch, int max_tokens, int 
                         tv[t * ORC_D + c] = src_elem(v_src, src_is_bf16, i);
                     }
                 int32_t phys = block_table[(size_t)b * max_pages + g];
-                orc_pack_page_m(tk, tv, ORC_D, kb, vb, kmode, pages + ((size_t)phys * H + h) * hp);
+                orc_pack_page_x(tk, tv, ORC_D, kb, vb, fmt, scale_of(scales, h, 0), scale_of(scales, h, 1),
+                                pages + ((size_t)phys * H + h) * hp);
             }
             for (int t = full * ORC_G; t < L; ++t)
                 for (int c = 0; c < ORC_D; ++c) {
@@ -409,12 +541,12 @@ int orc_pack_m(int kb, int vb, int kmode, int H, int batch, int max_tokens, int 
  * the write).  The token goes to residual slot pos mod 32; when that slot is 31 the 32
  * residual tokens form a full group and are quantized into page pos / 32.
  * k_new / v_new are bf16 [batch][H][128]. */
-int orc_append_m(int kb, int vb, int kmode, int H, int batch, const uint16_t *k_new, const uint16_t *v_new,
-                 const int32_t *pos, const int32_t *block_table, int max_pages,
+int orc_append_x(int kb, int vb, int fmt, const float *scales, int H, int batch, const uint16_t *k_new,
+                 const uint16_t *v_new, const int32_t *pos, const int32_t *block_table, int max_pages,
                  uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
 {
-    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
-    const size_t hp = orc_head_page_bytes(kb, vb);
+    if (!valid_format(kb, vb, fmt)) return 1;
+    const size_t hp = orc_head_page_bytes_x(kb, vb, fmt);
     static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
     for (int b = 0; b < batch; ++b) {
         int p = pos[b];
@@ -433,7 +565,8 @@ int orc_append_m(int kb, int vb, int kmode, int H, int batch, const uint16_t *k_
                     tv[i] = orc_bf16_to_f32(rv[i]);
                 }
                 int32_t phys = block_table[(size_t)b * max_pages + p / ORC_G];
-                orc_pack_page_m(tk, tv, ORC_D, kb, vb, kmode, pages + ((size_t)phys * H + h) * hp);
+                orc_pack_page_x(tk, tv, ORC_D, kb, vb, fmt, scale_of(scales, h, 0), scale_of(scales, h, 1),
+                                pages + ((size_t)phys * H + h) * hp);
             }
         }
     }
@@ -447,15 +580,15 @@ int orc_append_m(int kb, int vb, int kmode, int H, int batch, const uint16_t *k_
  *   lse = m + ln l,  out_c = sum_j exp(s_j - m) v_jc / l.
  * q is [batch][Hq][128] (bf16 or fp32); out is [batch][Hq][128]; lse is [batch][Hq]
  * (may be NULL). */
-int orc_decode_attn_m(int kb, int vb, int kmode, int Hq, int H, int batch, int q_is_bf16, const void *q,
-                      const int32_t *seq_len, const int32_t *block_table, int max_pages,
+int orc_decode_attn_x(int kb, int vb, int fmt, const float *scales, int Hq, int H, int batch, int q_is_bf16,
+                      const void *q, const int32_t *seq_len, const int32_t *block_table, int max_pages,
                       const uint8_t *pages, const uint16_t *resid_k, const uint16_t *resid_v,
                       double *out, double *lse)
 {
-    if (!valid_bits(kb) || !valid_bits(vb) || (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN)) return 1;
+    if (!valid_format(kb, vb, fmt)) return 1;
     if (H <= 0 || Hq % H != 0) return 3;
     const int G = Hq / H;
-    const size_t hp = orc_head_page_bytes(kb, vb);
+    const size_t hp = orc_head_page_bytes_x(kb, vb, fmt);
     for (int b = 0; b < batch; ++b) {
         int L = seq_len[b];
         if (L <= 0 || L > 32 * max_pages) return 2;
@@ -468,8 +601,9 @@ int orc_decode_attn_m(int kb, int vb, int kmode, int Hq, int H, int batch, int q
             /* this head's keys and values for all L tokens, as exact binary64 */
             for (int g = 0; g < full; ++g) {
                 int32_t phys = block_table[(size_t)b * max_pages + g];
-                orc_dequant_page_m(pages + ((size_t)phys * H + h) * hp, kb, vb, kmode,
-                                   K + (size_t)g * ORC_G * ORC_D, V + (size_t)g * ORC_G * ORC_D);
+                orc_dequant_page_x(pages + ((size_t)phys * H + h) * hp, kb, vb, fmt, scale_of(scales, h, 0),
+                                   scale_of(scales, h, 1), K + (size_t)g * ORC_G * ORC_D,
+                                   V + (size_t)g * ORC_G * ORC_D);
             }
             const uint16_t *rk = resid_k + ((size_t)b * H + h) * ORC_G * ORC_D;
             const uint16_t *rv = resid_v + ((size_t)b * H + h) * ORC_G * ORC_D;
@@ -504,6 +638,36 @@ int orc_decode_attn_m(int kb, int vb, int kmode, int Hq, int H, int batch, int q
         free(K); free(V); free(s);
     }
     return 0;
+}
+
+/* integer formats with a key mode */
+int orc_pack_m(int kb, int vb, int kmode, int H, int batch, int max_tokens, int src_is_bf16,
+               const void *k_src, const void *v_src, const int32_t *seq_len,
+               const int32_t *block_table, int max_pages,
+               uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+{
+    if (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN) return 1;
+    return orc_pack_x(kb, vb, kmode, NULL, H, batch, max_tokens, src_is_bf16, k_src, v_src, seq_len, block_table,
+                      max_pages, pages, resid_k, resid_v);
+}
+
+int orc_append_m(int kb, int vb, int kmode, int H, int batch, const uint16_t *k_new, const uint16_t *v_new,
+                 const int32_t *pos, const int32_t *block_table, int max_pages,
+                 uint8_t *pages, uint16_t *resid_k, uint16_t *resid_v)
+{
+    if (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN) return 1;
+    return orc_append_x(kb, vb, kmode, NULL, H, batch, k_new, v_new, pos, block_table, max_pages, pages, resid_k,
+                        resid_v);
+}
+
+int orc_decode_attn_m(int kb, int vb, int kmode, int Hq, int H, int batch, int q_is_bf16, const void *q,
+                      const int32_t *seq_len, const int32_t *block_table, int max_pages,
+                      const uint8_t *pages, const uint16_t *resid_k, const uint16_t *resid_v,
+                      double *out, double *lse)
+{
+    if (kmode != KMODE_CHANNEL && kmode != KMODE_TOKEN) return 1;
+    return orc_decode_attn_x(kb, vb, kmode, NULL, Hq, H, batch, q_is_bf16, q, seq_len, block_table, max_pages,
+                             pages, resid_k, resid_v, out, lse);
 }
 
 /* per-channel-key entry points (the library's default key mode) */

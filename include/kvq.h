@@ -57,6 +57,19 @@
  *   Residual: tokens 32*floor(L/32) .. L-1 of a sequence of length L are kept unquantized
  *   as bf16 in slot t mod 32 of resid_k / resid_v [batch][n_kv_heads][32][128].
  *
+ *   Floating-point layers (layer_format, below) store the values themselves, in the same
+ *   pages, block table and residual:
+ *     KVQ_LAYER_FP8:  head_page = 8192 bytes.  +0: K token-major [32][128] bytes,
+ *                     +4096: V channel-major [128][32] bytes.  Each byte is the OCP FP8
+ *                     E4M3 encoding of x / scale (binary32 divide; round to nearest even;
+ *                     finite values beyond 448 saturate to +-448), with one K scale and one
+ *                     V scale per KV head (fp8_scales); the stored value is byte * scale.
+ *     KVQ_LAYER_BF16: head_page = 16384 bytes.  +0: K token-major [32][128] bf16,
+ *                     +8192: V channel-major [128][32] bf16 (round to nearest even).
+ *   The pages keep precision-sensitive layers in BF16 and the rest in FP8 with per-layer
+ *   scaling.  [When should you use mixed-precision KV caching to preserve accuracy in
+ *   sensitive transformer layers (machinoai.in), sections 1-2]
+ *
  * Conventions.
  *   - Every device pointer is owned by the caller.  The library never allocates device
  *     memory, keeps no pointer after returning and has no mutable global state.
@@ -80,7 +93,7 @@
 extern "C" {
 #endif
 
-#define KVQ_FORMAT_VERSION 1
+#define KVQ_FORMAT_VERSION 2
 #define KVQ_HEAD_DIM 128
 #define KVQ_GROUP 32
 
@@ -104,10 +117,19 @@ typedef enum kvq_dtype { KVQ_BF16 = 0, KVQ_F32 = 1 } kvq_dtype;
 #define KVQ_KEYS_PER_CHANNEL 0
 #define KVQ_KEYS_PER_TOKEN 1
 
+/* Layer formats.  KVQ_LAYER_INT: integer codes at (k_bits, v_bits) in {2, 4, 8} with the
+ * layer's key mode.  KVQ_LAYER_FP8: E4M3 with per-head scales, k_bits = v_bits = 8.
+ * KVQ_LAYER_BF16: bfloat16, k_bits = v_bits = 16.  (Key modes apply to integer layers only.) */
+#define KVQ_LAYER_INT 0
+#define KVQ_LAYER_FP8 1
+#define KVQ_LAYER_BF16 2
+
 /* The per-layer precision table and the attention shape.  k_bits / v_bits are HOST
- * arrays of n_layers entries, each 2, 4 or 8.  k_mode is a HOST array of n_layers key
- * modes (KVQ_KEYS_PER_CHANNEL / KVQ_KEYS_PER_TOKEN), or NULL for per-channel keys in every
- * layer. */
+ * arrays of n_layers entries: 2, 4 or 8 for integer layers, 8 / 8 for FP8 layers and
+ * 16 / 16 for BF16 layers.  k_mode is a HOST array of n_layers key modes
+ * (KVQ_KEYS_PER_CHANNEL / KVQ_KEYS_PER_TOKEN), or NULL for per-channel keys in every layer.
+ * layer_format is a HOST array of n_layers KVQ_LAYER_* values, or NULL for integer codes in
+ * every layer. */
 typedef struct kvq_model {
     int32_t n_layers;
     int32_t n_q_heads;
@@ -116,6 +138,7 @@ typedef struct kvq_model {
     const uint8_t *k_bits;
     const uint8_t *v_bits;
     const uint8_t *k_mode;     /* optional, see above */
+    const uint8_t *layer_format; /* optional, see above */
 } kvq_model;
 
 /* One layer's cache (all device pointers). */
@@ -127,6 +150,9 @@ typedef struct kvq_layer_cache {
     const int32_t *block_table;/* int32 [batch][max_pages]                                  */
     int32_t batch;
     int32_t max_pages;
+    const float *fp8_scales;   /* FP8 layers: fp32 [n_kv_heads][2] = (K scale, V scale) of
+                                  each KV head, positive, finite and normal; NULL = all 1.0.
+                                  Ignored by the other formats.                             */
 } kvq_layer_cache;
 
 /* Status name, e.g. "KVQ_ERR_WORKSPACE". */
@@ -135,14 +161,17 @@ const char *kvq_status_str(kvq_status s);
 /* KVQ_FORMAT_VERSION of the built library. */
 int32_t kvq_format_version(void);
 
-/* Bytes of one page of one KV head: 512 * (kb + vb + 2); 0 for unsupported widths. */
+/* Bytes of one page of one KV head of an integer layer: 512 * (kb + vb + 2); 0 for
+ * unsupported widths. */
 size_t kvq_head_page_bytes(int32_t k_bits, int32_t v_bits);
 
-/* Bytes of one page of layer `layer` for all KV heads; 0 on invalid arguments. */
+/* Bytes of one page of layer `layer` for all KV heads, in the layer's format (integer,
+ * FP8: 8192 per head, BF16: 16384 per head); 0 on invalid arguments. */
 size_t kvq_page_bytes(const kvq_model *model, int32_t layer);
 
 /* Equivalent bit-width of the table: mean over layers of (k_bits + v_bits) / 2, counting
- * code bits only (K8V4 is 6, the Llama table with layers 0-2 and 31 at K4V8 is 3.25).
+ * code bits only (K8V4 is 6, the Llama table with layers 0-2 and 31 at K4V8 is 3.25; FP8
+ * layers count 8, BF16 layers 16).
  * [KVTuner OpenReview discussion, reply to reviewer 1, section 2]  Returns -1 on invalid
  * arguments. */
 double kvq_equiv_bits(const kvq_model *model);

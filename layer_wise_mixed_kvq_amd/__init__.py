@@ -17,36 +17,50 @@ import ctypes
 from typing import Optional, Sequence
 
 from . import _native
-from ._native import KVQ_BF16, KVQ_F32, KvqError, KvqLayerCache, KvqModel, check, lib
+from ._native import (KVQ_BF16, KVQ_F32, KVQ_LAYER_BF16, KVQ_LAYER_FP8, KVQ_LAYER_INT, KvqError, KvqLayerCache,
+                      KvqModel, check, lib)
 
 HEAD_DIM = 128
 GROUP = 32
 
-__all__ = ["Model", "KEYS_PER_CHANNEL", "KEYS_PER_TOKEN", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
+__all__ = ["Model", "KEYS_PER_CHANNEL", "KEYS_PER_TOKEN", "LAYER_INT", "LAYER_FP8", "LAYER_BF16", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_head_page_bytes",
            "kvq_page_bytes", "kvq_equiv_bits", "kvq_format_version", "lib"]
 
 
 KEYS_PER_CHANNEL, KEYS_PER_TOKEN = 0, 1
+LAYER_INT, LAYER_FP8, LAYER_BF16 = KVQ_LAYER_INT, KVQ_LAYER_FP8, KVQ_LAYER_BF16
 
 
 class Model:
     """Per-layer table plus the attention shape (kvq_model).  Each entry of `pairs` is
-    (key bits, value bits) for per-channel keys, or (key bits, value bits, key mode) with
-    key mode "channel" / "token" (or KEYS_PER_CHANNEL / KEYS_PER_TOKEN)."""
+    (key bits, value bits) for integer codes with per-channel keys, (key bits, value bits,
+    key mode) with key mode "channel" / "token" (or KEYS_PER_CHANNEL / KEYS_PER_TOKEN), or
+    "fp8" / "bf16" for a layer stored as FP8 E4M3 (scaled per KV head) or BF16."""
 
-    def __init__(self, pairs: Sequence[tuple], n_q_heads: int, n_kv_heads: int, head_dim: int = HEAD_DIM):
+    def __init__(self, pairs: Sequence, n_q_heads: int, n_kv_heads: int, head_dim: int = HEAD_DIM):
         modes = {"channel": KEYS_PER_CHANNEL, "token": KEYS_PER_TOKEN, KEYS_PER_CHANNEL: KEYS_PER_CHANNEL,
                  KEYS_PER_TOKEN: KEYS_PER_TOKEN}
-        self.pairs = [(int(e[0]), int(e[1])) for e in pairs]
-        self.k_modes = [modes[e[2]] if len(e) > 2 else KEYS_PER_CHANNEL for e in pairs]
+        floats = {"fp8": (8, 8, LAYER_FP8), "bf16": (16, 16, LAYER_BF16)}
+        self.pairs, self.k_modes, self.formats = [], [], []
+        for e in pairs:
+            if isinstance(e, str):
+                kb, vb, fmt = floats[e]
+                self.pairs.append((kb, vb))
+                self.k_modes.append(KEYS_PER_CHANNEL)
+                self.formats.append(fmt)
+            else:
+                self.pairs.append((int(e[0]), int(e[1])))
+                self.k_modes.append(modes[e[2]] if len(e) > 2 else KEYS_PER_CHANNEL)
+                self.formats.append(LAYER_INT)
         n = len(self.pairs)
         self._kb = (ctypes.c_uint8 * max(n, 1))(*[k for k, _ in self.pairs])
         self._vb = (ctypes.c_uint8 * max(n, 1))(*[v for _, v in self.pairs])
         self._km = (ctypes.c_uint8 * max(n, 1))(*self.k_modes)
+        self._fmt = (ctypes.c_uint8 * max(n, 1))(*self.formats)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         self.c = KvqModel(n, n_q_heads, n_kv_heads, head_dim, ctypes.cast(self._kb, u8p),
-                          ctypes.cast(self._vb, u8p), ctypes.cast(self._km, u8p))
+                          ctypes.cast(self._vb, u8p), ctypes.cast(self._km, u8p), ctypes.cast(self._fmt, u8p))
         self.n_layers, self.n_q_heads, self.n_kv_heads, self.head_dim = n, n_q_heads, n_kv_heads, head_dim
 
     @property
@@ -76,19 +90,27 @@ def kvq_equiv_bits(model: Model) -> float:
 class LayerCache:
     """Device buffers of one layer (kvq_layer_cache).
 
-    pages       uint8 [n_pages][n_kv_heads][head page bytes of this layer's pair]
+    pages       uint8 [n_pages][n_kv_heads][head page bytes of this layer's format]
     resid_k/v   bfloat16 [batch][n_kv_heads][32][128]
     block_table int32 [batch][max_pages]; pass one tensor to every layer to share it.
+    fp8_scales  FP8 layers: float32 [n_kv_heads][2] (K scale, V scale) on the device, or
+                None for 1.0; ignored by the other formats.
     """
 
     def __init__(self, model: Model, layer: int, batch: int, max_pages: int,
-                 n_pages: Optional[int] = None, block_table=None, device="cuda"):
+                 n_pages: Optional[int] = None, block_table=None, device="cuda", fp8_scales=None):
         import torch
-        kb, vb = model.pairs[layer]
         self.layer = layer
         self.batch, self.max_pages = batch, max_pages
         self.n_pages = batch * max_pages if n_pages is None else n_pages
-        hp = kvq_head_page_bytes(kb, vb)
+        hp = kvq_page_bytes(model, layer) // model.n_kv_heads
+        if hp == 0:
+            raise KvqError(_native.KVQ_ERR_UNSUPPORTED, f"layer {layer} of the model")
+        if fp8_scales is not None:
+            if fp8_scales.dtype != torch.float32 or tuple(fp8_scales.shape) != (model.n_kv_heads, 2):
+                raise ValueError("fp8_scales must be float32 [n_kv_heads][2]")
+            _dev(fp8_scales, "fp8_scales")
+        self.fp8_scales = fp8_scales
         self.pages = torch.zeros((self.n_pages, model.n_kv_heads, hp), dtype=torch.uint8, device=device)
         self.resid_k = torch.zeros((batch, model.n_kv_heads, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=device)
         self.resid_v = torch.zeros_like(self.resid_k)
@@ -107,12 +129,13 @@ class LayerCache:
         v.pages = self.pages
         v.resid_k, v.resid_v = self.resid_k[b0:b1], self.resid_v[b0:b1]
         v.block_table = self.block_table[b0:b1]
+        v.fp8_scales = self.fp8_scales
         return v
 
     def c_struct(self) -> KvqLayerCache:
         return KvqLayerCache(self.pages.data_ptr(), self.n_pages, self.resid_k.data_ptr(),
                              self.resid_v.data_ptr(), self.block_table.data_ptr(), self.batch,
-                             self.max_pages)
+                             self.max_pages, self.fp8_scales.data_ptr() if self.fp8_scales is not None else None)
 
 
 def _stream(stream):

@@ -11,6 +11,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so"
 
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGNMENT, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(6)
 KVQ_BF16, KVQ_F32 = 0, 1
+KVQ_LAYER_INT, KVQ_LAYER_FP8, KVQ_LAYER_BF16 = 0, 1, 2
 
 EXPORTED = ("kvq_status_str", "kvq_format_version", "kvq_head_page_bytes", "kvq_page_bytes",
             "kvq_equiv_bits", "kvq_validate_model", "kvq_pack", "kvq_append",
@@ -21,14 +22,14 @@ class KvqModel(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("k_bits", ctypes.POINTER(ctypes.c_uint8)), ("v_bits", ctypes.POINTER(ctypes.c_uint8)),
-                ("k_mode", ctypes.POINTER(ctypes.c_uint8))]
+                ("k_mode", ctypes.POINTER(ctypes.c_uint8)), ("layer_format", ctypes.POINTER(ctypes.c_uint8))]
 
 
 class KvqLayerCache(ctypes.Structure):
     _fields_ = [("pages", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
                 ("resid_k", ctypes.c_void_p), ("resid_v", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("batch", ctypes.c_int32),
-                ("max_pages", ctypes.c_int32)]
+                ("max_pages", ctypes.c_int32), ("fp8_scales", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):

@@ -12,7 +12,7 @@ LIB = os.path.join(PKG, "libkvq.so")
 # (source, extra flags): the decode kernels build in one translation unit per key bit width
 UNITS = [("kvq_api.hip", []), ("kvq_quant.hip", []), ("kvq_decode.hip", ["-DKVQ_DECODE_COMMON"]),
          ("kvq_decode.hip", ["-DKVQ_DECODE_KB=2"]), ("kvq_decode.hip", ["-DKVQ_DECODE_KB=4"]),
-         ("kvq_decode.hip", ["-DKVQ_DECODE_KB=8"])]
+         ("kvq_decode.hip", ["-DKVQ_DECODE_KB=8"]), ("kvq_decode.hip", ["-DKVQ_DECODE_KB=16"])]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include "../../include/kvq.h"
+#include "kvq_codec.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -25,14 +26,46 @@ kvq_status check_model(const kvq_model *m)
     if (m->n_q_heads / m->n_kv_heads > kvq::decode_max_g()) return KVQ_ERR_UNSUPPORTED;
     if (m->n_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
     for (int l = 0; l < m->n_layers; ++l) {
-        if (!valid_bits(m->k_bits[l]) || !valid_bits(m->v_bits[l])) return KVQ_ERR_UNSUPPORTED;
-        if (m->k_mode && m->k_mode[l] != KVQ_KEYS_PER_CHANNEL && m->k_mode[l] != KVQ_KEYS_PER_TOKEN)
+        const int fmt = m->layer_format ? m->layer_format[l] : KVQ_LAYER_INT;
+        if (fmt == KVQ_LAYER_FP8) {
+            if (m->k_bits[l] != 8 || m->v_bits[l] != 8) return KVQ_ERR_UNSUPPORTED;
+        } else if (fmt == KVQ_LAYER_BF16) {
+            if (m->k_bits[l] != 16 || m->v_bits[l] != 16) return KVQ_ERR_UNSUPPORTED;
+        } else if (fmt == KVQ_LAYER_INT) {
+            if (!valid_bits(m->k_bits[l]) || !valid_bits(m->v_bits[l])) return KVQ_ERR_UNSUPPORTED;
+            if (m->k_mode && m->k_mode[l] != KVQ_KEYS_PER_CHANNEL && m->k_mode[l] != KVQ_KEYS_PER_TOKEN)
+                return KVQ_ERR_UNSUPPORTED;
+        } else {
             return KVQ_ERR_UNSUPPORTED;
+        }
     }
     return KVQ_OK;
 }
 
-int key_mode(const kvq_model *m, int layer) { return m->k_mode ? m->k_mode[layer] : KVQ_KEYS_PER_CHANNEL; }
+int layer_format(const kvq_model *m, int layer) { return m->layer_format ? m->layer_format[layer] : KVQ_LAYER_INT; }
+
+// the kernels' layer code: integer key mode 0 / 1, FP8 2, BF16 3
+int layer_code(const kvq_model *m, int layer)
+{
+    const int fmt = layer_format(m, layer);
+    if (fmt == KVQ_LAYER_FP8) return kvq::kLayerFp8;
+    if (fmt == KVQ_LAYER_BF16) return kvq::kLayerBf16;
+    return m->k_mode ? m->k_mode[layer] : KVQ_KEYS_PER_CHANNEL;
+}
+
+size_t head_page_bytes_of(const kvq_model *m, int layer)
+{
+    const int fmt = layer_format(m, layer);
+    if (fmt == KVQ_LAYER_FP8) return static_cast<size_t>(kvq::FloatLayout<kvq::kLayerFp8>::kBytes);
+    if (fmt == KVQ_LAYER_BF16) return static_cast<size_t>(kvq::FloatLayout<kvq::kLayerBf16>::kBytes);
+    return static_cast<size_t>(kvq::head_page_bytes(m->k_bits[layer], m->v_bits[layer]));
+}
+
+// the FP8 scales the kernels read for this layer (null: 1.0, and for every other format)
+const float *scales_of(const kvq_model *m, int layer, const kvq_layer_cache *c)
+{
+    return layer_format(m, layer) == KVQ_LAYER_FP8 ? c->fp8_scales : nullptr;
+}
 
 kvq_status check_layer(const kvq_model *m, int32_t layer, const kvq_layer_cache *c)
 {
@@ -43,6 +76,7 @@ kvq_status check_layer(const kvq_model *m, int32_t layer, const kvq_layer_cache 
     if (c->batch <= 0 || c->batch > 65535 || c->max_pages <= 0 || c->n_pages <= 0) return KVQ_ERR_INVALID_ARG;
     if (c->n_pages > (int64_t)INT32_MAX) return KVQ_ERR_UNSUPPORTED;
     if (!aligned16(c->pages) || !aligned16(c->resid_k) || !aligned16(c->resid_v)) return KVQ_ERR_ALIGNMENT;
+    if (c->fp8_scales && (reinterpret_cast<uintptr_t>(c->fp8_scales) & 3u)) return KVQ_ERR_ALIGNMENT;
     return KVQ_OK;
 }
 
@@ -92,8 +126,7 @@ size_t kvq_head_page_bytes(int32_t k_bits, int32_t v_bits)
 size_t kvq_page_bytes(const kvq_model *model, int32_t layer)
 {
     if (check_model(model) != KVQ_OK || layer < 0 || layer >= model->n_layers) return 0;
-    return static_cast<size_t>(model->n_kv_heads) *
-           kvq_head_page_bytes(model->k_bits[layer], model->v_bits[layer]);
+    return static_cast<size_t>(model->n_kv_heads) * head_page_bytes_of(model, layer);
 }
 
 double kvq_equiv_bits(const kvq_model *model)
@@ -125,12 +158,13 @@ kvq_status kvq_pack(const kvq_model *model, int32_t layer, const kvq_layer_cache
     p.pages = cache->pages;
     p.resid_k = cache->resid_k;
     p.resid_v = cache->resid_v;
+    p.scales = scales_of(model, layer, cache);
     p.n_pages = cache->n_pages;
     p.H = model->n_kv_heads;
     p.batch = cache->batch;
     p.max_tokens = max_tokens;
     p.max_pages = cache->max_pages;
-    return hip_status(kvq::launch_pack(model->k_bits[layer], model->v_bits[layer], key_mode(model, layer), p,
+    return hip_status(kvq::launch_pack(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                        src_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
 }
 
@@ -149,11 +183,12 @@ kvq_status kvq_append(const kvq_model *model, int32_t layer, const kvq_layer_cac
     p.pages = cache->pages;
     p.resid_k = cache->resid_k;
     p.resid_v = cache->resid_v;
+    p.scales = scales_of(model, layer, cache);
     p.n_pages = cache->n_pages;
     p.H = model->n_kv_heads;
     p.batch = cache->batch;
     p.max_pages = cache->max_pages;
-    return hip_status(kvq::launch_append(model->k_bits[layer], model->v_bits[layer], key_mode(model, layer), p,
+    return hip_status(kvq::launch_append(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -204,6 +239,7 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     p.pages = cache->pages;
     p.resid_k = cache->resid_k;
     p.resid_v = cache->resid_v;
+    p.scales = scales_of(model, layer, cache);
     p.out = out;
     p.lse = lse;
     p.part_o = reinterpret_cast<float *>(w + ws.part_o_off);
@@ -217,7 +253,7 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     p.max_seq_len = max_seq_len;
     p.pages_per_split = pps;
     p.n_splits = n_splits;
-    return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], key_mode(model, layer), p,
+    return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                          q_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
 }
 

@@ -156,6 +156,124 @@ __device__ void quantize_page(QuantSmem &sm, uint8_t *__restrict__ dst)
     }
 }
 
+// ------------------------------------------------------------------------------------
+// floating-point layer formats: FP8 (OCP E4M3) and BF16
+// ------------------------------------------------------------------------------------
+// A layer may store K and V as x / scale in E4M3 (one K and one V scale per KV head) or as
+// bfloat16, instead of integer codes.  [When should you use mixed-precision KV caching to
+// preserve accuracy in sensitive transformer layers (machinoai.in), sections 1-2]
+// Head page: K token-major [32][128] elements, then V channel-major [128][32].
+// Layer codes: how one layer's pages are stored.
+constexpr int kLayerKeysPerChannel = 0, kLayerKeysPerToken = 1;   // integer codes, key mode
+constexpr int kLayerFp8 = 2, kLayerBf16 = 3;                       // floating point
+
+constexpr bool is_float_layer(int km) { return km == kLayerFp8 || km == kLayerBf16; }
+
+template <int FMT>
+struct FloatLayout {
+    static constexpr int kElem = FMT == kLayerFp8 ? 1 : 2;            // bytes per element
+    static constexpr int kV = kGroup * kHeadDim * kElem;              // V section offset
+    static constexpr int kBytes = 2 * kV;
+};
+
+// bytes of one head page of a layer with bit widths (KB, VB) and layer code KM
+template <int KB, int VB, int KM>
+constexpr int layer_page_bytes()
+{
+    if constexpr (is_float_layer(KM))
+        return FloatLayout<KM>::kBytes;
+    else
+        return PageLayout<KB, VB>::kBytes;
+}
+
+// E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; no infinities; S.1111.111
+// is NaN; largest finite 448.  Round to nearest even; finite values beyond 448 saturate.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x)
+{
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (a == 0.0f) return sign;
+    if (a != a) return sign | 0x7Fu;
+    if (a > 3.0e38f) return sign | 0x7Eu;
+    int e;
+    frexpf(a, &e);
+    int E = e - 1;
+    if (E < -6) E = -6;                                   // subnormal spacing 2^-9
+    float n = __builtin_rintf(ldexpf(a, 3 - E));          // exact scaling, then ties to even
+    if (n == 0.0f) return sign;
+    if (n >= 16.0f) {
+        n *= 0.5f;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && n > 14.0f)) return sign | 0x7Eu;
+    const uint32_t ni = static_cast<uint32_t>(n);
+    if (ni < 8u) return sign | ni;
+    return sign | (static_cast<uint32_t>(E + 7) << 3) | (ni - 8u);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b)
+{
+    const int e = (b >> 3) & 15, m = b & 7;
+    const float v = e ? ldexpf(static_cast<float>(8 + m), e - 10) : ldexpf(static_cast<float>(m), -9);
+    return (b & 0x80u) ? -v : v;
+}
+
+// Convert the staged tiles of one page-head into `dst` (global) in format FMT.  All 256
+// threads call it; every output dword is built from tile elements no other thread reads,
+// so with DEQUANT the tiles are overwritten in place with the values the page stores
+// (E4M3 value * scale, binary32), valid after the workgroup's next barrier.
+template <int FMT, bool DEQUANT = false>
+__device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, float ks, float vs)
+{
+#pragma clang fp contract(off)
+    using FL = FloatLayout<FMT>;
+    const int tid = threadIdx.x;
+    uint32_t *k32 = reinterpret_cast<uint32_t *>(dst);
+    uint32_t *v32 = reinterpret_cast<uint32_t *>(dst + FL::kV);
+    constexpr int kPer = 4 / FL::kElem;                                // elements per dword
+    constexpr int kWords = kGroup * kHeadDim / kPer;
+    for (int d = tid; d < kWords; d += kCodecThreads) {
+        // K: token-major
+        {
+            const int t = d / (kHeadDim / kPer), c0 = (d % (kHeadDim / kPer)) * kPer;
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                float &x = sm.k[t * kTileStride + c0 + i];
+                if constexpr (FMT == kLayerFp8) {
+                    const uint32_t b = f32_to_e4m3(x / ks);
+                    w |= b << (8 * i);
+                    if constexpr (DEQUANT) x = e4m3_to_f32(b) * ks;
+                } else {
+                    const uint32_t b = float_to_bf16_bits(x);
+                    w |= b << (16 * i);
+                    if constexpr (DEQUANT) x = bf16_bits_to_float(static_cast<uint16_t>(b));
+                }
+            }
+            k32[d] = w;
+        }
+        // V: channel-major
+        {
+            const int c = d / (kGroup / kPer), t0 = (d % (kGroup / kPer)) * kPer;
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                float &x = sm.v[(t0 + i) * kTileStride + c];
+                if constexpr (FMT == kLayerFp8) {
+                    const uint32_t b = f32_to_e4m3(x / vs);
+                    w |= b << (8 * i);
+                    if constexpr (DEQUANT) x = e4m3_to_f32(b) * vs;
+                } else {
+                    const uint32_t b = float_to_bf16_bits(x);
+                    w |= b << (16 * i);
+                    if constexpr (DEQUANT) x = bf16_bits_to_float(static_cast<uint16_t>(b));
+                }
+            }
+            v32[d] = w;
+        }
+    }
+}
+
 }  // namespace kvq
 
 #endif  // KVQ_CODEC_H

@@ -39,6 +39,16 @@
 // h / 4 of the accumulator: with G <= 4 every lane holds exactly one head per token.
 //   scores:  D[head][token]   = A(q s hi|lo, from LDS)    x B(key codes, token-major rows)
 //   values:  D[head][channel] = A(p s hi|lo, from LDS)    x B(value codes, chunk layout)
+//
+// Floating-point layers (FP8 E4M3 with one K and one V scale per KV head, or BF16) hold
+// the values themselves, so nothing is folded per page: the scales multiply the scores
+// and the output once.  FP8 bytes convert exactly to normal fp16 values (v_cvt_scalef32_
+// pk_f16_fp8 at scale 1) and meet the same fp16 hi|lo A operands; BF16 pages go to the
+// bf16 matrix-core instruction with A split into three bf16 parts (24 significant bits).
+// The contraction order inside one MFMA is free, so each lane takes 32 consecutive
+// channels of a token row (one or two 16-byte loads) and A is laid out to match.
+//   [When should you use mixed-precision KV caching to preserve accuracy in sensitive
+//    transformer layers (machinoai.in), sections 1-2]
 #include "kvq_codec.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -56,9 +66,30 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float4_t mfma(const uint4 &a, const uint4 &b, const float4_t &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4_t mfma_bf16(const uint4 &a, const uint4 &b, const float4_t &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+// Eight E4M3 bytes (two words, byte i = element i) as eight fp16 values: exact, since every
+// E4M3 value is zero or a normal fp16 value.
+__device__ __forceinline__ uint4 fp8x8_to_f16(uint32_t w0, uint32_t w1)
+{
+    const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                      __builtin_bit_cast(uint32_t, d));
 }
 
 // hi / lo split of two products x0*y0, x1*y1 into packed fp16 pairs with hi + lo equal to
@@ -78,6 +109,25 @@ __device__ __forceinline__ uint32_t split_lo(float x0, float y0, float x1, float
     const float r0 = fmaf(x0, y0, -half_bits_to_float(hi & 0xFFFFu));
     const float r1 = fmaf(x1, y1, -half_bits_to_float(hi >> 16));
     return __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(r0), static_cast<_Float16>(r1)});
+}
+
+// Two values as a packed bf16 pair (round to nearest even) and the residuals x - bf16(x),
+// exact in binary32.  Three such steps give hi + mid + lo equal to x to 24 bits.
+__device__ __forceinline__ uint32_t bf16_pair(float x0, float x1, float &r0, float &r1)
+{
+    uint32_t h = __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(x0), static_cast<__bf16>(x1)});
+    __asm__ volatile("" : "+v"(h));
+    r0 = x0 - __uint_as_float(h << 16);
+    r1 = x1 - __uint_as_float(h & 0xFFFF0000u);
+    return h;
+}
+
+__device__ __forceinline__ void split3_bf16(float x0, float x1, uint32_t &hi, uint32_t &mid, uint32_t &lo)
+{
+    float r0, r1, e0, e1;
+    hi = bf16_pair(x0, x1, r0, r1);
+    mid = bf16_pair(r0, r1, e0, e1);
+    lo = bf16_pair(e0, e1, r0, r1);
 }
 
 // LDS ordering inside one wave: the LDS executes one wave's DS instructions in issue
@@ -175,7 +225,10 @@ __device__ __forceinline__ uint32_t fp16x2_1024()
 template <int BITS>
 __device__ __forceinline__ constexpr int unpack_shift(int j)
 {
-    return BITS * (j % (8 / BITS));
+    if constexpr (BITS > 8)
+        return 0;     // not a code width (floating-point layers)
+    else
+        return BITS * (j % (8 / BITS));
 }
 
 template <int BITS>
@@ -205,12 +258,17 @@ __device__ __forceinline__ int key_pair_channel(int jj, int j)
     return nd * (k / n) + (k % n);
 }
 
-template <int GS>
+// A-operand parts: fp16 hi | lo, or bf16 hi | mid | lo for BF16 layers
+constexpr int a_parts(int km) { return km == kLayerBf16 ? 3 : 2; }
+
+template <int GS, int KM>
 struct WaveLds {
+    static constexpr int NP = a_parts(KM);
+    static constexpr int PG = is_float_layer(KM) ? 1 : 4;   // value groups with their own scales
     // rows padded by 4 words so that the 128-bit A-operand reads of different head rows
     // fall into different LDS banks
-    alignas(16) uint32_t qp[2][4 * GS + 1][68];      // (q s) hi / lo pairs: [part][head, + zero row][pair]
-    alignas(16) uint32_t pp[2][4][4 * GS + 1][20];   // (p s) hi / lo pairs: [part][value group][head][pair]
+    alignas(16) uint32_t qp[NP][4 * GS + 1][68];     // (q s) parts: [part][head, + zero row][pair]
+    alignas(16) uint32_t pp[NP][PG][4 * GS + 1][20]; // (p s) parts: [part][value group][head][pair]
     float p[32][4 * GS];                             // softmax weights of the page: [token][head]
     float alpha[4 * GS];
     float bv[4][4 * GS];                             // value zero terms at the end: [group][head]
@@ -243,13 +301,13 @@ struct CombineLds {
     float l[kMergeChunk][16];
 };
 
-template <int GS>
+template <int GS, int KM>
 struct DecodeSmem {
     float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128)
     int eq[4 * GS];               // per head: |qs * 2^eq| in [1, 2)
     ResidualOut<GS> ro;
     union {
-        WaveLds<GS> w[kWaves];
+        WaveLds<GS, KM> w[kWaves];
         MergeLds<GS> merge;
         ResidualLds<GS> res;
         CombineLds comb;
@@ -309,8 +367,8 @@ __device__ __forceinline__ void load_residual(const DecodeParams &p, long long b
 // completes a group (flush) the 32 rows are quantized into their page `flush_page` (same
 // codec and bytes as kvq_append) and the tile is replaced by its dequantized values, which
 // are then attended.  Returns false if the flush page id is outside the pool.
-template <int KB, int VB, int GS, bool KT>
-__device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, const uint4 (&kv)[4], int nres, int G,
+template <int KB, int VB, int GS, int KM>
+__device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS, KM> &sm, const uint4 (&kv)[4], int nres, int G,
                                 long long bh, bool append, bool flush, int flush_page)
 {
     ResidualLds<GS> &R = sm.u.res;
@@ -340,8 +398,12 @@ __device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS> &sm, const
         ok = phys >= 0 && phys < p.n_pages;
         if (ok) {
             uint8_t *dst = static_cast<uint8_t *>(p.pages) +
-                           (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
-            quantize_page<KB, VB, true, KT>(R.q, dst);
+                           (static_cast<long long>(phys) * p.H + h) * layer_page_bytes<KB, VB, KM>();
+            if constexpr (is_float_layer(KM))
+                quantize_page_float<KM, true>(R.q, dst, p.scales ? p.scales[2 * h] : 1.0f,
+                                              p.scales ? p.scales[2 * h + 1] : 1.0f);
+            else
+                quantize_page<KB, VB, true, KM == kLayerKeysPerToken>(R.q, dst);
         }
         __syncthreads();
     }
@@ -398,10 +460,47 @@ struct PageRegs {
     uint32_t vszw[2];        // value (s, z) of the two tokens this lane folds into p
 };
 
-template <int KB, int VB, bool KT>
+// Floating-point layers: kc[blk] holds channels 32a .. 32a+31 of token 16*blk + r16 (one
+// element per byte for FP8, two per word for BF16) and vc holds, for each channel block nb,
+// tokens 8a .. 8a+7 of channel 16*nb + r16 (vc[2nb..] for FP8, vc[4nb..] for BF16).
+template <int KM, int NK, int NV>
+__device__ __forceinline__ void load_page_float(uint32_t (&kc)[2][NK], uint32_t (&vc)[NV], const uint8_t *base,
+                                                int lane)
+{
+    using FL = FloatLayout<KM>;
+    constexpr int E = FL::kElem;
+    const int a = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(base + (16 * blk + r16) * kHeadDim * E + 32 * a * E);
+#pragma unroll
+        for (int i = 0; i < 2 * E; ++i) {
+            const uint4 x = src[i];
+            kc[blk][4 * i] = x.x; kc[blk][4 * i + 1] = x.y; kc[blk][4 * i + 2] = x.z; kc[blk][4 * i + 3] = x.w;
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+        const uint8_t *src = base + FL::kV + (16 * nb + r16) * kGroup * E + 8 * a * E;
+        if constexpr (E == 1) {
+            const uint2 x = *reinterpret_cast<const uint2 *>(src);
+            vc[2 * nb] = x.x; vc[2 * nb + 1] = x.y;
+        } else {
+            const uint4 x = *reinterpret_cast<const uint4 *>(src);
+            vc[4 * nb] = x.x; vc[4 * nb + 1] = x.y; vc[4 * nb + 2] = x.z; vc[4 * nb + 3] = x.w;
+        }
+    }
+}
+
+template <int KB, int VB, int KM>
 __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *base, int lane, int ch0, int ch1,
                                           int t0, int t1)
 {
+    if constexpr (is_float_layer(KM)) {
+        load_page_float<KM>(r.kc, r.vc, base, lane);
+        return;
+    } else {
+    constexpr bool KT = KM == kLayerKeysPerToken;
     using PL = PageLayout<KB, VB>;
     const int a = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -436,15 +535,19 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
     const uint32_t *vsz = reinterpret_cast<const uint32_t *>(base + PL::kVSz);
     r.vszw[0] = vsz[kValueGroups * t0 + a];
     r.vszw[1] = vsz[kValueGroups * t1 + a];
+    }
 }
 
-// KT: per-token keys (one key group per token and 32 channels) instead of per-channel keys
-template <int KB, int VB, int GS, typename QT, bool KT>
+// KM: the layer code -- integer codes with per-channel or per-token keys (one key group per
+// token and 32 channels), or FP8 / BF16 values
+template <int KB, int VB, int GS, typename QT, int KM>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 {
-    using PL = PageLayout<KB, VB>;
+    constexpr bool KT = KM == kLayerKeysPerToken;
+    constexpr bool FLT = is_float_layer(KM);
+    constexpr int kPageBytes = layer_page_bytes<KB, VB, KM>();
     constexpr int HS = 4 * GS;                 // head slots
-    __shared__ DecodeSmem<GS> sm;
+    __shared__ DecodeSmem<GS, KM> sm;
     // grid (H, batch, splits): the split index varies slowest, so every (sequence, KV head)
     // has its split 0 dispatched first
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
@@ -500,8 +603,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
     // per-channel keys: any channel pair of the lane's 32-channel group; per-token keys: the
     // pair 32*kjj + 8*kq + 2*kj, + 1, so that matrix-core block kjj is exactly key group kjj
-    const int ch0 = KT ? 32 * kjj + 8 * kq + 2 * kj : 32 * kq + key_pair_channel<KB>(kjj, kj);
-    const int ch1 = KT ? ch0 + 1 : ch0 + 16 / KB;
+    // floating-point layers: the natural pair 2*lane, 2*lane + 1
+    const int ch0 = FLT ? 2 * lane : KT ? 32 * kjj + 8 * kq + 2 * kj : 32 * kq + key_pair_channel<KB>(kjj, kj);
+    const int ch1 = FLT || KT ? ch0 + 1 : ch0 + 16 / KB;
     const int t0 = 8 * (r16 >> 2) + (r16 & 3), t1 = t0 + 4;   // value pair this lane folds (group a)
     // powers of two the code unpack leaves on this lane's key channels / value tokens
     const int kshift = unpack_shift<KB>(kj), vshift = unpack_shift<VB>(r16 & 3);
@@ -512,10 +616,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     if (id_bad) my_phys = 0;
     auto page_base = [&](int j) -> const uint8_t * {
         const int phys = __builtin_amdgcn_readlane(my_phys, j);
-        return pool + (static_cast<long long>(phys) * p.H + h) * PL::kBytes;
+        return pool + (static_cast<long long>(phys) * p.H + h) * kPageBytes;
     };
     PageRegs<KB, VB> cur, nxt;
-    if (n_my > 0) load_page<KB, VB, KT>(cur, page_base(0), lane, ch0, ch1, t0, t1);
+    if (n_my > 0) load_page<KB, VB, KM>(cur, page_base(0), lane, ch0, ch1, t0, t1);
 #pragma unroll
     for (int k = 0; k < kQPer; ++k) {
         const int i = tid + k * kThreads;
@@ -537,12 +641,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 
     const long long slot0 = bh * p.n_splits;
     if (n_ps > 0) {
-        WaveLds<GS> &W = sm.u.w[wave];
-        for (int i = lane; i < 64; i += 64) {      // zero rows: A operands of absent heads
-            W.qp[0][HS][i] = 0u;
-            W.qp[1][HS][i] = 0u;
-            W.pp[0][i / 16][HS][i % 16] = 0u;
-            W.pp[1][i / 16][HS][i % 16] = 0u;
+        WaveLds<GS, KM> &W = sm.u.w[wave];
+        constexpr int NP = WaveLds<GS, KM>::NP, PG = WaveLds<GS, KM>::PG;
+#pragma unroll
+        for (int part = 0; part < NP; ++part) {     // zero rows: A operands of absent heads
+            W.qp[part][HS][lane] = 0u;
+            if (lane < 16 * PG) W.pp[part][lane / 16][HS][lane % 16] = 0u;
         }
         const int hr = 4 * (r16 & 3) + (r16 >> 2);             // head of A row r16
         const int arow = hr < G ? hr : HS;                      // zero row when absent
@@ -585,6 +689,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             }
             wave_lds_sync();
         }
+        // floating-point layers: A = q~ (FP8: times 2^14, fp16 hi | lo; BF16: three bf16
+        // parts) for the pair 2*lane, 2*lane + 1, folded once; the scores take the K scale
+        const float ks = FLT && p.scales ? p.scales[2 * h] : 1.0f;
+        const float vs = FLT && p.scales ? p.scales[2 * h + 1] : 1.0f;
+        float ksc[GS];                                          // score factor per head slot
+        if constexpr (FLT) {
+#pragma unroll
+            for (int hh = 0; hh < HS; ++hh) {
+                if constexpr (KM == kLayerFp8) {
+                    const uint32_t hi = split_hi(qw[hh][0] * 16384.0f, qw[hh][1] * 16384.0f);
+                    W.qp[0][hh][lane] = hi;
+                    W.qp[1][hh][lane] = split_lo(qw[hh][0], 16384.0f, qw[hh][1], 16384.0f, hi);
+                } else {
+                    split3_bf16(qw[hh][0], qw[hh][1], W.qp[0][hh][lane], W.qp[1][hh][lane], W.qp[2][hh][lane]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < GS; ++i) ksc[i] = KM == kLayerFp8 ? inv_eq[i] * (ks * (1.0f / 16384.0f)) : inv_eq[i];
+            wave_lds_sync();
+        }
 
         const uint32_t magic = fp16x2_1024();
         float4_t acc[8];
@@ -606,7 +730,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 
         auto process_page = [&](const PageRegs<KB, VB> &cur) {
           float s2[2][GS];
-          if constexpr (!KT) {
+          if constexpr (FLT) {
+            // ---- floating-point keys: q~ against the stored values, then the K scale ------
+            float4_t sacc[2];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                uint4 av[NP];
+#pragma unroll
+                for (int part = 0; part < NP; ++part) av[part] = lds_read16(&W.qp[part][arow][16 * a + 4 * jj]);
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) {
+                    float4_t c = jj == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : sacc[blk];
+                    if constexpr (KM == kLayerFp8) {
+                        const uint4 bk = fp8x8_to_f16(cur.kc[blk][2 * jj], cur.kc[blk][2 * jj + 1]);
+                        c = mfma(av[0], bk, c);
+                        c = mfma(av[1], bk, c);
+                    } else {
+                        const uint4 bk = make_uint4(cur.kc[blk][4 * jj], cur.kc[blk][4 * jj + 1], cur.kc[blk][4 * jj + 2],
+                                                    cur.kc[blk][4 * jj + 3]);
+                        c = mfma_bf16(av[0], bk, c);
+                        c = mfma_bf16(av[1], bk, c);
+                        c = mfma_bf16(av[2], bk, c);
+                    }
+                    sacc[blk] = c;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < GS; ++i)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = sacc[blk][i] * ksc[i];
+          } else if constexpr (!KT) {
             // ---- page exponent: |q~ s 2^E| < 2^15 for every channel ---------------
             uint32_t smax = 0;
 #pragma unroll
@@ -706,11 +859,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     l_part[i] *= alpha[i];
 #pragma unroll
                     for (int nb = 0; nb < 8; ++nb) acc[nb][i] *= alpha[i];
-                    if (r16 == 0) W.alpha[4 * i + a] = alpha[i];
+                    if (!FLT && r16 == 0) W.alpha[4 * i + a] = alpha[i];
                 }
-                wave_lds_sync();
+                if constexpr (!FLT) {
+                    wave_lds_sync();
 #pragma unroll
-                for (int hh = 0; hh < HS; ++hh) zb[hh] *= W.alpha[hh];
+                    for (int hh = 0; hh < HS; ++hh) zb[hh] *= W.alpha[hh];
+                }
             }
 #pragma unroll
             for (int i = 0; i < GS; ++i) {
@@ -721,6 +876,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     W.p[16 * blk + r16][4 * i + a] = pv;
                 }
             }
+          if constexpr (FLT) {
+            // ---- floating-point values: A = p (FP8: times 2^14, fp16 hi | lo; BF16: three
+            // bf16 parts) for token pair r16 of the lane's heads; the V scale comes at the end
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < GS; ++i) {
+                const int hh = 4 * i + a;
+                const float p0 = W.p[2 * r16][hh], p1 = W.p[2 * r16 + 1][hh];
+                if constexpr (KM == kLayerFp8) {
+                    const uint32_t hi = split_hi(p0 * 16384.0f, p1 * 16384.0f);
+                    W.pp[0][0][hh][r16] = hi;
+                    W.pp[1][0][hh][r16] = split_lo(p0, 16384.0f, p1, 16384.0f, hi);
+                } else {
+                    split3_bf16(p0, p1, W.pp[0][0][hh][r16], W.pp[1][0][hh][r16], W.pp[2][0][hh][r16]);
+                }
+            }
+            wave_lds_sync();
+            uint4 av[NP];
+#pragma unroll
+            for (int part = 0; part < NP; ++part) av[part] = lds_read16(&W.pp[part][0][arow][4 * a]);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                if constexpr (KM == kLayerFp8) {
+                    const uint4 bv = fp8x8_to_f16(cur.vc[2 * nb], cur.vc[2 * nb + 1]);
+                    acc[nb] = mfma(av[0], bv, acc[nb]);
+                    acc[nb] = mfma(av[1], bv, acc[nb]);
+                } else {
+                    const uint4 bv = make_uint4(cur.vc[4 * nb], cur.vc[4 * nb + 1], cur.vc[4 * nb + 2], cur.vc[4 * nb + 3]);
+                    acc[nb] = mfma_bf16(av[0], bv, acc[nb]);
+                    acc[nb] = mfma_bf16(av[1], bv, acc[nb]);
+                    acc[nb] = mfma_bf16(av[2], bv, acc[nb]);
+                }
+            }
+          } else {
             // ---- value-scale exponent of this page -----------------------------------
             {
                 uint32_t vmax = max(cur.vszw[0] & 0x7FFFu, cur.vszw[1] & 0x7FFFu);
@@ -766,13 +955,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     acc[nb] = mfma(alo, bv, acc[nb]);
                 }
             }
+          }
         };
         // two page buffers in fixed roles: page j+1 is in flight while page j is processed.
         // Every prefetch is unconditional (past the wave's last page it reloads that page,
         // an L2 hit), so the compiler's wait counts see one path and wait only for the page
         // about to be used, never for the one just requested.
         auto prefetch = [&](PageRegs<KB, VB> &dst, int j) {
-            load_page<KB, VB, KT>(dst, page_base(min(j, n_my - 1)), lane, ch0, ch1, t0, t1);
+            load_page<KB, VB, KM>(dst, page_base(min(j, n_my - 1)), lane, ch0, ch1, t0, t1);
         };
         int j = 0;
         for (; j + 1 < n_my; j += 2) {
@@ -787,20 +977,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         float lw[GS];
 #pragma unroll
         for (int i = 0; i < GS; ++i) lw[i] = row_sum(l_part[i]);
+        if constexpr (!FLT) {
 #pragma unroll
-        for (int hh = 0; hh < HS; ++hh) {
-            const float v = row_sum(zb[hh]);    // lanes of group a cover all 32 tokens once
-            if (r16 == 0) W.bv[a][hh] = v;
+            for (int hh = 0; hh < HS; ++hh) {
+                const float v = row_sum(zb[hh]);    // lanes of group a cover all 32 tokens once
+                if (r16 == 0) W.bv[a][hh] = v;
+            }
+            wave_lds_sync();
         }
-        wave_lds_sync();
         float o_out[8][GS];
-        const float unscale = ldexpf(1.0f, -ev);
+        if constexpr (FLT) {
+            const float unscale = KM == kLayerFp8 ? vs * (1.0f / 16384.0f) : 1.0f;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
+            for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(acc[nb][i], unscale, W.bv[nb >> 1][4 * i + a]);
+                for (int i = 0; i < GS; ++i) o_out[nb][i] = acc[nb][i] * unscale;
+        } else {
+            const float unscale = ldexpf(1.0f, -ev);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(acc[nb][i], unscale, W.bv[nb >> 1][4 * i + a]);
+        }
         __syncthreads();     // every wave is done with its WaveLds: reuse the space
-        if (has_res) bad_page |= !residual_tokens<KB, VB, GS, KT>(p, sm, res_kv, nres, G, bh, append, flush, full);
+        if (has_res) bad_page |= !residual_tokens<KB, VB, GS, KM>(p, sm, res_kv, nres, G, bh, append, flush, full);
         MergeLds<GS> &M = sm.u.merge;
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
@@ -815,7 +1015,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             }
         }
     } else if (has_res) {
-        bad_page |= !residual_tokens<KB, VB, GS, KT>(p, sm, res_kv, nres, G, bh, append, flush, full);
+        bad_page |= !residual_tokens<KB, VB, GS, KM>(p, sm, res_kv, nres, G, bh, append, flush, full);
     }
 
     // ---- this workgroup's merge: its waves' page states and, on the last split, the residual
@@ -970,29 +1170,32 @@ __global__ void zero_fill_kernel(uint32_t *p, size_t n_words)
 }
 #endif
 
-template <int KB, int VB, int GS, bool KT>
+template <int KB, int VB, int GS, int KM>
 hipError_t launch_decode_g(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
     dim3 grid(p.H, p.batch, p.n_splits);
     if (q_f32)
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float, KT>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float, KM>), grid, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t, KT>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t, KM>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <int KB, int VB, bool KT>
+template <int KB, int VB, int KM>
 hipError_t launch_decode_k(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
-    if (p.G <= 4) return launch_decode_g<KB, VB, 1, KT>(p, q_f32, s);
-    if (p.G <= 8) return launch_decode_g<KB, VB, 2, KT>(p, q_f32, s);
-    return launch_decode_g<KB, VB, 4, KT>(p, q_f32, s);
+    if (p.G <= 4) return launch_decode_g<KB, VB, 1, KM>(p, q_f32, s);
+    if (p.G <= 8) return launch_decode_g<KB, VB, 2, KM>(p, q_f32, s);
+    return launch_decode_g<KB, VB, 4, KM>(p, q_f32, s);
 }
 
+// integer layers: key mode 0 / 1
 template <int KB, int VB>
 hipError_t launch_decode_t(int kmode, const DecodeParams &p, bool q_f32, hipStream_t s)
 {
-    return kmode ? launch_decode_k<KB, VB, true>(p, q_f32, s) : launch_decode_k<KB, VB, false>(p, q_f32, s);
+    if (kmode == kLayerKeysPerChannel) return launch_decode_k<KB, VB, kLayerKeysPerChannel>(p, q_f32, s);
+    if (kmode == kLayerKeysPerToken) return launch_decode_k<KB, VB, kLayerKeysPerToken>(p, q_f32, s);
+    return hipErrorInvalidValue;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1000,16 +1203,23 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
 // This source is compiled once per key bit width (KVQ_DECODE_KB = 2, 4, 8: the kernels of
-// that width) and once with KVQ_DECODE_COMMON (host helpers and the dispatch), so that the
+// that width, FP8 with 8; 16: BF16) and once with KVQ_DECODE_COMMON (host helpers and the dispatch), so that the
 // kernel instantiations build in parallel.
 #if defined(KVQ_DECODE_KB)
 #define KVQ_LAUNCH_KB_NAME_(KBV) launch_decode_kb##KBV
 #define KVQ_LAUNCH_KB_NAME(KBV) KVQ_LAUNCH_KB_NAME_(KBV)
 hipError_t KVQ_LAUNCH_KB_NAME(KVQ_DECODE_KB)(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s)
 {
+#if KVQ_DECODE_KB == 16
+    if (vb == 16 && kmode == kLayerBf16) return launch_decode_k<16, 16, kLayerBf16>(p, q_f32, s);
+#else
+#if KVQ_DECODE_KB == 8
+    if (vb == 8 && kmode == kLayerFp8) return launch_decode_k<8, 8, kLayerFp8>(p, q_f32, s);
+#endif
     if (vb == 2) return launch_decode_t<KVQ_DECODE_KB, 2>(kmode, p, q_f32, s);
     if (vb == 4) return launch_decode_t<KVQ_DECODE_KB, 4>(kmode, p, q_f32, s);
     if (vb == 8) return launch_decode_t<KVQ_DECODE_KB, 8>(kmode, p, q_f32, s);
+#endif
     return hipErrorInvalidValue;
 }
 #endif
@@ -1046,6 +1256,7 @@ hipError_t launch_decode(int kb, int vb, int kmode, const DecodeParams &p, bool 
     if (kb == 2) return launch_decode_kb2(vb, kmode, p, q_f32, s);
     if (kb == 4) return launch_decode_kb4(vb, kmode, p, q_f32, s);
     if (kb == 8) return launch_decode_kb8(vb, kmode, p, q_f32, s);
+    if (kb == 16) return launch_decode_kb16(vb, kmode, p, q_f32, s);
     return hipErrorInvalidValue;
 }
 

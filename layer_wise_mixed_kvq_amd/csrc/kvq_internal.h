@@ -14,6 +14,7 @@ struct PackParams {
     void *pages;
     uint16_t *resid_k;
     uint16_t *resid_v;
+    const float *scales;  // FP8 layers: [H][2] K / V scale, or null (1.0)
     long long n_pages;
     int H;
     int batch;
@@ -29,6 +30,7 @@ struct AppendParams {
     void *pages;
     uint16_t *resid_k;
     uint16_t *resid_v;
+    const float *scales;  // FP8 layers: [H][2] K / V scale, or null (1.0)
     long long n_pages;
     int H;
     int batch;
@@ -45,6 +47,7 @@ struct DecodeParams {
     void *pages;                 // written only by the fused append's page flush
     uint16_t *resid_k;           // written only by the fused append (the new token's slot)
     uint16_t *resid_v;
+    const float *scales;         // FP8 layers: [H][2] K / V scale, or null (1.0)
     float *out;
     float *lse;
     float *part_o;        // [batch][H][n_splits][G][128]
@@ -67,7 +70,8 @@ struct DecodeWorkspace {
 DecodeWorkspace decode_workspace_layout(int batch, int H, int G, int n_splits);
 int decode_default_pages_per_split(int batch, int H, int max_full_pages);
 
-// kmode: 0 = per-channel keys, 1 = per-token keys
+// kmode: the layer code -- 0 = integer codes with per-channel keys, 1 = integer codes with
+// per-token keys, 2 = FP8 E4M3 (kb = vb = 8), 3 = BF16 (kb = vb = 16)
 hipError_t launch_pack(int kb, int vb, int kmode, const PackParams &p, bool src_f32, hipStream_t s);
 hipError_t launch_append(int kb, int vb, int kmode, const AppendParams &p, hipStream_t s);
 hipError_t launch_decode(int kb, int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
@@ -75,6 +79,7 @@ hipError_t launch_decode(int kb, int vb, int kmode, const DecodeParams &p, bool 
 hipError_t launch_decode_kb2(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
 hipError_t launch_decode_kb4(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
 hipError_t launch_decode_kb8(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
+hipError_t launch_decode_kb16(int vb, int kmode, const DecodeParams &p, bool q_f32, hipStream_t s);
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t s);
 
 }  // namespace kvq

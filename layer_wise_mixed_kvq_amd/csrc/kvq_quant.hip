@@ -10,7 +10,11 @@
 //
 // One workgroup of 256 threads quantizes one page of one KV head: the 32 x 128 K and V
 // tiles are staged in LDS as binary32 (coalesced 8/16-byte loads, 16 threads per 256-byte
-// token row), then the page codec of kvq_codec.h encodes and packs them.
+// token row), then the page codec of kvq_codec.h encodes and packs them.  Layers kept in
+// FP8 (E4M3 of x / scale, one K and one V scale per KV head) or BF16 go through the
+// floating-point page codec instead.
+//   [When should you use mixed-precision KV caching to preserve accuracy in sensitive
+//    transformer layers (machinoai.in), sections 1-2]
 #include "kvq_codec.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -66,8 +70,19 @@ __device__ void stage_tile(const SrcT *__restrict__ src, long long row_stride, f
     }
 }
 
+// One page-head from the staged tiles, in the layer's format (KM: layer code).
+template <int KB, int VB, int KM>
+__device__ __forceinline__ void encode_page(QuantSmem &sm, uint8_t *pages, const float *scales, int phys, int H, int h)
+{
+    uint8_t *dst = pages + (static_cast<long long>(phys) * H + h) * layer_page_bytes<KB, VB, KM>();
+    if constexpr (is_float_layer(KM))
+        quantize_page_float<KM>(sm, dst, scales ? scales[2 * h] : 1.0f, scales ? scales[2 * h + 1] : 1.0f);
+    else
+        quantize_page<KB, VB, false, KM == kLayerKeysPerToken>(sm, dst);
+}
+
 // grid: (pages covering max_tokens, n_kv_heads, batch)
-template <int KB, int VB, bool KTOK, typename SrcT>
+template <int KB, int VB, int KM, typename SrcT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 {
     __shared__ QuantSmem sm;
@@ -86,9 +101,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
         stage_tile<SrcT>(ks + base, row_stride, sm.k);
         stage_tile<SrcT>(vs + base, row_stride, sm.v);
         __syncthreads();
-        uint8_t *dst = static_cast<uint8_t *>(p.pages) +
-                       (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
-        quantize_page<KB, VB, false, KTOK>(sm, dst);
+        encode_page<KB, VB, KM>(sm, static_cast<uint8_t *>(p.pages), p.scales, phys, p.H, h);
     } else if (g == full) {
         // trailing L mod 32 tokens -> bf16 residual slots 0 .. L mod 32 - 1
         const int nres = L - full * kGroup;
@@ -104,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 }
 
 // grid: (n_kv_heads, batch)
-template <int KB, int VB, bool KTOK>
+template <int KB, int VB, int KM>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p)
 {
     __shared__ QuantSmem sm;
@@ -132,43 +145,51 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p)
         sm.v[t * kTileStride + c] = bf16_bits_to_float(vb16);
     }
     __syncthreads();
-    uint8_t *dst = static_cast<uint8_t *>(p.pages) + (static_cast<long long>(phys) * p.H + h) * PageLayout<KB, VB>::kBytes;
-    quantize_page<KB, VB, false, KTOK>(sm, dst);
+    encode_page<KB, VB, KM>(sm, static_cast<uint8_t *>(p.pages), p.scales, phys, p.H, h);
 }
 
-template <int KB, int VB, bool KTOK>
+template <int KB, int VB, int KM>
 hipError_t launch_pack_m(const PackParams &p, bool src_f32, hipStream_t s)
 {
     const int gx = (p.max_tokens + kGroup - 1) / kGroup;
     if (gx == 0) return hipSuccess;
     dim3 grid(gx, p.H, p.batch);
     if (src_f32)
-        hipLaunchKernelGGL((pack_kernel<KB, VB, KTOK, float>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((pack_kernel<KB, VB, KM, float>), grid, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((pack_kernel<KB, VB, KTOK, uint16_t>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((pack_kernel<KB, VB, KM, uint16_t>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int KB, int VB, int KM>
+hipError_t launch_append_m(const AppendParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL((append_kernel<KB, VB, KM>), dim3(p.H, p.batch), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 template <int KB, int VB>
 hipError_t launch_pack_t(int kmode, const PackParams &p, bool src_f32, hipStream_t s)
 {
-    return kmode ? launch_pack_m<KB, VB, true>(p, src_f32, s) : launch_pack_m<KB, VB, false>(p, src_f32, s);
+    if (kmode == kLayerKeysPerChannel) return launch_pack_m<KB, VB, kLayerKeysPerChannel>(p, src_f32, s);
+    if (kmode == kLayerKeysPerToken) return launch_pack_m<KB, VB, kLayerKeysPerToken>(p, src_f32, s);
+    return hipErrorInvalidValue;
 }
 
 template <int KB, int VB>
 hipError_t launch_append_t(int kmode, const AppendParams &p, hipStream_t s)
 {
-    if (kmode)
-        hipLaunchKernelGGL((append_kernel<KB, VB, true>), dim3(p.H, p.batch), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL((append_kernel<KB, VB, false>), dim3(p.H, p.batch), dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+    if (kmode == kLayerKeysPerChannel) return launch_append_m<KB, VB, kLayerKeysPerChannel>(p, s);
+    if (kmode == kLayerKeysPerToken) return launch_append_m<KB, VB, kLayerKeysPerToken>(p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_pack(int kb, int vb, int kmode, const PackParams &p, bool src_f32, hipStream_t s)
 {
+    if (kb == 8 && vb == 8 && kmode == kLayerFp8) return launch_pack_m<8, 8, kLayerFp8>(p, src_f32, s);
+    if (kb == 16 && vb == 16 && kmode == kLayerBf16) return launch_pack_m<16, 16, kLayerBf16>(p, src_f32, s);
 #define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_pack_t<KBV, VBV>(kmode, p, src_f32, s)
     KVQ_P(2, 2); KVQ_P(2, 4); KVQ_P(2, 8);
     KVQ_P(4, 2); KVQ_P(4, 4); KVQ_P(4, 8);
@@ -179,6 +200,8 @@ hipError_t launch_pack(int kb, int vb, int kmode, const PackParams &p, bool src_
 
 hipError_t launch_append(int kb, int vb, int kmode, const AppendParams &p, hipStream_t s)
 {
+    if (kb == 8 && vb == 8 && kmode == kLayerFp8) return launch_append_m<8, 8, kLayerFp8>(p, s);
+    if (kb == 16 && vb == 16 && kmode == kLayerBf16) return launch_append_m<16, 16, kLayerBf16>(p, s);
 #define KVQ_P(KBV, VBV) if (kb == KBV && vb == VBV) return launch_append_t<KBV, VBV>(kmode, p, s)
     KVQ_P(2, 2); KVQ_P(2, 4); KVQ_P(2, 8);
     KVQ_P(4, 2); KVQ_P(4, 4); KVQ_P(4, 8);

@@ -33,10 +33,13 @@ class Case:
     """One layer's seeded inputs plus its oracle cache and its device cache."""
 
     def __init__(self, kb, vb, H, G, lens, *, seed=1, layer=0, src="bf16", q_dtype="bf16", shuffle=True,
-                 extra_pages=3, n_outliers=3, spare_pages_per_seq=0, kmode=0):
+                 extra_pages=3, n_outliers=3, spare_pages_per_seq=0, kmode=0, scales=None):
         import torch
         self.kb, self.vb, self.H, self.G = kb, vb, H, G
-        self.kmode = kmode            # 0: per-channel keys, 1: per-token keys
+        # the oracle's layer format: 0 / 1 integer codes with per-channel / per-token keys,
+        # 2 FP8 E4M3 (kb = vb = 8, scales [H][2] or None for 1.0), 3 BF16 (kb = vb = 16)
+        self.kmode = kmode
+        self.scales = None if scales is None else np.ascontiguousarray(scales, dtype=np.float32).reshape(H, 2)
         self.lens = np.array(lens, dtype=np.int32)
         self.B = len(lens)
         self.T = max(1, int(self.lens.max()))
@@ -53,22 +56,28 @@ class Case:
 
     # ---- oracle side -------------------------------------------------------------
     def oracle_pack(self, orc):
-        self.o_pages, self.o_rk, self.o_rv = orc.new_cache(self.kb, self.vb, self.H, self.B, self.n_phys)
+        self.o_pages, self.o_rk, self.o_rv = orc.new_cache(self.kb, self.vb, self.H, self.B, self.n_phys,
+                                                           self.kmode)
         orc.pack(self.kb, self.vb, host_array(self.k), host_array(self.v), self.lens, self.bt,
-                 self.o_pages, self.o_rk, self.o_rv, kmode=self.kmode)
+                 self.o_pages, self.o_rk, self.o_rv, kmode=self.kmode, scales=self.scales)
 
     def oracle_decode(self, orc, lens=None):
         lens = self.lens if lens is None else np.asarray(lens, dtype=np.int32)
         return orc.decode_attn(self.kb, self.vb, self.H, host_array(self.q), lens, self.bt, self.o_pages,
-                               self.o_rk, self.o_rv, kmode=self.kmode)
+                               self.o_rk, self.o_rv, kmode=self.kmode, scales=self.scales)
+
+    def layer_entry(self):
+        """This layer's entry in a device Model table."""
+        return {2: "fp8", 3: "bf16"}.get(self.kmode, (self.kb, self.vb, self.kmode))
 
     # ---- device side -------------------------------------------------------------
     def device_setup(self, kvq):
         import torch
-        self.model = kvq.Model([(self.kb, self.vb, self.kmode)], self.H * self.G, self.H)
+        self.model = kvq.Model([self.layer_entry()], self.H * self.G, self.H)
         self.bt_d = torch.from_numpy(self.bt).to(self.dev)
+        self.scales_d = None if self.scales is None else torch.from_numpy(self.scales).to(self.dev)
         self.cache = kvq.LayerCache(self.model, 0, self.B, self.maxp, n_pages=self.n_phys,
-                                    block_table=self.bt_d, device=self.dev)
+                                    block_table=self.bt_d, device=self.dev, fp8_scales=self.scales_d)
         self.lens_d = torch.from_numpy(self.lens).to(self.dev)
 
     def device_pack(self, kvq):

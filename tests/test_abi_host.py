@@ -36,7 +36,7 @@ def test_header_symbols_exported(kvq):
 
 
 def test_format_constants(kvq):
-    assert kvq.kvq_format_version() == 1
+    assert kvq.kvq_format_version() == 2
     for kb in (2, 4, 8):
         for vb in (2, 4, 8):
             assert kvq.kvq_head_page_bytes(kb, vb) == 512 * (kb + vb + 2)
@@ -56,6 +56,27 @@ def test_equiv_bits_and_page_bytes(kvq):
     assert kvq.kvq_page_bytes(m, 5) == 8 * 512 * 8
     assert kvq.kvq_page_bytes(m, 28) == 8 * 512 * 6
     assert kvq.kvq_page_bytes(m, 32) == 0
+
+
+def test_float_layer_formats(kvq):
+    """FP8 / BF16 layers: page bytes 8192 / 16384 per KV head, equivalent bits 8 / 16, the
+    machinoai page's 8 BF16 + 24 FP8 example at 10 bits, and width checks per format."""
+    from layer_wise_mixed_kvq_amd import _native as N
+    mix = kvq.Model(["bf16"] * 8 + ["fp8"] * 24, 32, 8)
+    assert kvq.lib().kvq_validate_model(ctypes.byref(mix.c)) == N.KVQ_OK
+    assert kvq.kvq_page_bytes(mix, 0) == 8 * 16384
+    assert kvq.kvq_page_bytes(mix, 8) == 8 * 8192
+    assert kvq.kvq_equiv_bits(mix) == (8 * 16 + 24 * 8) / 32
+    # integer and float layers side by side
+    m = kvq.Model([(4, 2), "fp8", (2, 2, "token"), "bf16"], 8, 2)
+    assert [kvq.kvq_page_bytes(m, l) for l in range(4)] == [2 * 512 * 8, 2 * 8192, 2 * 512 * 6, 2 * 16384]
+    # FP8 needs 8 / 8 and BF16 16 / 16; unknown format codes are rejected
+    for fmt, kb, vb in [(N.KVQ_LAYER_FP8, 4, 8), (N.KVQ_LAYER_FP8, 16, 16), (N.KVQ_LAYER_BF16, 8, 8),
+                        (N.KVQ_LAYER_INT, 16, 16), (3, 4, 4)]:
+        bad = kvq.Model([(kb, vb)], 4, 1)
+        bad._fmt[0] = fmt
+        assert kvq.lib().kvq_validate_model(ctypes.byref(bad.c)) == N.KVQ_ERR_UNSUPPORTED, (fmt, kb, vb)
+        assert kvq.kvq_page_bytes(bad, 0) == 0
 
 
 def _status(kvq, fn, *args):

@@ -33,6 +33,23 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
 LLAMA_C325 = [(4, 8)] * 3 + [(4, 2)] * 24 + [(2, 2)] * 4 + [(4, 8)]
 QWEN_C40 = [(8, 4)] * 4 + [(4, 4)] * 4 + [(4, 2)] * 16 + [(8, 4)] * 4
+# the machinoai page's 32-layer example: 8 sensitive layers kept in BF16, 24 in FP8; the
+# sensitive ones here are the boundary layers (first four and last four)
+BF16_FP8_MIX = ["bf16"] * 4 + ["fp8"] * 24 + ["bf16"] * 4
+# FP8 scales per (layer, KV head): the synthetic data's bound over 448 (K: |x| < 60 with the
+# x10 outlier channels, V: |x| < 6)
+FP8_SCALES = (60.0 / 448.0, 6.0 / 448.0)
+
+
+def layer_spec(entry, k_mode=0):
+    """(key bits, value bits, oracle format code, head-page bytes) of one table entry:
+    (kb, vb) integer codes, "fp8" or "bf16"."""
+    if entry == "fp8":
+        return 8, 8, 2, 8192
+    if entry == "bf16":
+        return 16, 16, 3, 16384
+    kb, vb = entry
+    return kb, vb, k_mode, 512 * (kb + vb + 2)
 
 CONFIGS = {
     "llama": dict(workload="llama3.1-8b-shape C3.25 decode step (append + attention, 32 layers)",
@@ -55,6 +72,12 @@ CONFIGS = {
                             "(append + attention, 32 layers)",
                    pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=16, context=4096, n_outliers=3,
                    seed=20250204, k_mode=1),
+    "bf16fp8": dict(workload="llama3.1-8b-shape BF16/FP8 per-layer mix (layers 0-3 and 28-31 BF16, 4-27 FP8 "
+                             "E4M3 with per-head scales) decode step (append + attention, 32 layers)",
+                    pairs=BF16_FP8_MIX, n_q_heads=32, n_kv_heads=8, batch=16, context=4096, n_outliers=3,
+                    seed=20250208),
+    "formats": dict(workload="llama3.1-8b shape, B=16, 4096 cached tokens, 32 layers: decode step tokens/s of "
+                             "all-BF16, calibrated all-FP8, the 8 BF16 + 24 FP8 mix and the C3.25 integer table"),
     "copy": dict(workload="streaming copy: 1 GiB int32 read + 1 GiB written (torch bitwise_not)"),
     "sweep": dict(workload="uniform-pair sweep, llama3.1-8b shape, 32 layers: decode step tokens/s per table "
                            "relative to KV8 at the (batch, input length) points of the pages' throughput table "
@@ -100,12 +123,14 @@ def decode_alg_bytes(kb, vb, batch, H, Hq, L):
     return ragged_decode_alg_bytes(kb, vb, [L] * batch, H, Hq)
 
 
-def ragged_decode_alg_bytes(kb, vb, lens, H, Hq):
-    """As decode_alg_bytes, for sequences attending over lens[b] tokens each."""
+def ragged_decode_alg_bytes(kb, vb, lens, H, Hq, head_page=None):
+    """As decode_alg_bytes, for sequences attending over lens[b] tokens each (head_page:
+    bytes of one page of one KV head, default the integer layout of (kb, vb))."""
+    hp = 512 * (kb + vb + 2) if head_page is None else head_page
     tot = 0
     for L in lens:
         full, nres = int(L) // 32, int(L) % 32
-        tot += H * full * 512 * (kb + vb + 2) + H * nres * 128 * 2 * 2
+        tot += H * full * hp + H * nres * 128 * 2 * 2
     return tot + len(lens) * Hq * 128 * (2 + 4) + len(lens) * Hq * 4
 
 
@@ -133,7 +158,9 @@ class DecodeStack:
         self.kvq = kvq
         pairs = cfg["pairs"]
         self.k_mode = cfg.get("k_mode", 0)       # 0: per-channel keys, 1: per-token keys
-        self.model = kvq.Model([(kb, vb, self.k_mode) for kb, vb in pairs], cfg["n_q_heads"], cfg["n_kv_heads"])
+        self.specs = [layer_spec(e, self.k_mode) for e in pairs]
+        self.model = kvq.Model([e if isinstance(e, str) else (e[0], e[1], self.k_mode) for e in pairs],
+                               cfg["n_q_heads"], cfg["n_kv_heads"])
         B, H = cfg["batch"], cfg["n_kv_heads"]
         seed = cfg["seed"]
         if "ragged" in cfg:
@@ -160,9 +187,10 @@ class DecodeStack:
         # sequences per pack chunk: bounded source bytes (K and V)
         per_tok = H * 128 * (4 if src_dtype == "f32" else 2) * 2
         order = np.arange(B)
+        fp8_scales = torch.tensor([FP8_SCALES] * H, dtype=torch.float32, device=device)
         for l, _ in enumerate(pairs):
             cache = kvq.LayerCache(self.model, l, B, self.max_pages, n_pages=n_phys, block_table=self.block_table,
-                                   device=device)
+                                   device=device, fp8_scales=fp8_scales if self.specs[l][2] == 2 else None)
             cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
             b0 = 0
             while b0 < B:
@@ -214,7 +242,7 @@ class DecodeStack:
         return tot
 
     def decode_bytes(self):
-        return [ragged_decode_alg_bytes(kb, vb, self.attend, self.H, self.Hq) for kb, vb in self.cfg["pairs"]]
+        return [ragged_decode_alg_bytes(kb, vb, self.attend, self.H, self.Hq, hp) for kb, vb, _, hp in self.specs]
 
 
 def capture(fn):
@@ -276,7 +304,9 @@ def cpu_baseline_decode(cfg, stack, n_seq):
     seed, H, Hq = cfg["seed"], cfg["n_kv_heads"], cfg["n_q_heads"]
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
     t_total, attended = 0.0, 0
-    for l, (kb, vb) in enumerate(cfg["pairs"]):
+    for l, entry in enumerate(cfg["pairs"]):
+        kb, vb, km, _ = layer_spec(entry, cfg.get("k_mode", 0))
+        scales = np.array([FP8_SCALES] * H, dtype=np.float32) if km == 2 else None
         cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
         for b in range(n_seq):
             C = int(stack.lens[b])
@@ -287,12 +317,11 @@ def cpu_baseline_decode(cfg, stack, n_seq):
             kn = synth.fill(seed, synth.KIND_K_NEW, l, 1, 1, H, b0=b, chan_mult=cm).view(1, H, 128)
             vn = synth.fill(seed, synth.KIND_V_NEW, l, 1, 1, H, b0=b).view(1, H, 128)
             q = synth.fill(seed, synth.KIND_Q, l, 1, 1, Hq, b0=b).view(1, Hq, 128)
-            km = cfg.get("k_mode", 0)
-            pages, rk, rv = orc.new_cache(kb, vb, H, 1, maxp)
-            orc.pack(kb, vb, bits(k), bits(v), [C], bt, pages, rk, rv, kmode=km)
+            pages, rk, rv = orc.new_cache(kb, vb, H, 1, maxp, km)
+            orc.pack(kb, vb, bits(k), bits(v), [C], bt, pages, rk, rv, kmode=km, scales=scales)
             t0 = time.perf_counter()
-            orc.append(kb, vb, bits(kn), bits(vn), [C], bt, pages, rk, rv, kmode=km)
-            orc.decode_attn(kb, vb, H, bits(q), [C + 1], bt, pages, rk, rv, kmode=km)
+            orc.append(kb, vb, bits(kn), bits(vn), [C], bt, pages, rk, rv, kmode=km, scales=scales)
+            orc.decode_attn(kb, vb, H, bits(q), [C + 1], bt, pages, rk, rv, kmode=km, scales=scales)
             t_total += time.perf_counter() - t0
             attended += C + 1
     return t_total, attended
@@ -329,6 +358,8 @@ def main():
         return bench_copy(args)
     if args.config == "sweep":
         return bench_sweep(args)
+    if args.config == "formats":
+        return bench_formats(args)
 
     log(f"[bench] building {args.config} cache ...")
     t0 = time.perf_counter()
@@ -399,7 +430,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16-in/fp32-acc, int2/4/8 codes",
+        "dtype": stack_dtype(stack),
         "data": "synthetic (seeded Irwin-Hall N(0,1) K/V/q, 3 outlier key channels x10 per layer and head)",
         "config": {"workload": cfg["workload"], "batch": stack.B, "context": stack.C,
                    "attended_tokens": stack.L, "mean_attended_tokens": float(stack.attend.mean()), "layers": n_layers, "n_q_heads": stack.Hq,
@@ -420,6 +451,49 @@ def main():
                      "alg_bytes_per_launch": sum(dbytes) / n_layers},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(rec), flush=True)
+
+
+def stack_dtype(stack):
+    kinds = sorted({("fp8 e4m3" if s[2] == 2 else "bf16" if s[2] == 3 else "int2/4/8 codes") for s in stack.specs})
+    return "bf16-in/fp32-acc, " + " + ".join(kinds)
+
+
+FORMAT_TABLES = {"BF16": ["bf16"] * 32, "FP8": ["fp8"] * 32, "BF16/FP8 mix": BF16_FP8_MIX, "C3.25": LLAMA_C325}
+
+
+def bench_formats(args):
+    """The machinoai page's comparison at kernel level: all-BF16, calibrated all-FP8 and the
+    8 BF16 + 24 FP8 mix (plus the C3.25 integer table) on one shape: decode step tokens/s,
+    KV bytes per step and the decode kernel's GB/s."""
+    import torch
+    dev = torch.device("cuda:0")
+    res = {}
+    for name, pairs in FORMAT_TABLES.items():
+        cfg = dict(CONFIGS["bf16fp8"], pairs=pairs)
+        stack = DecodeStack(cfg, dev)
+        g = capture(lambda: stack.step(True))
+        ms, _ = time_graph(g, args.steps, args.warmup)
+        g_attn = capture(lambda: stack.step(False))
+        ms_attn, _ = time_graph(g_attn, args.steps, 2)
+        kv = sum(stack.decode_bytes())
+        res[name] = {"tokens_per_s": stack.B * 1000.0 / ms, "ms_per_step": ms, "decode_bytes_per_step": kv,
+                     "decode_gbps": kv / (ms_attn * 1e-3) / 1e9, "equiv_bits": stack.kvq.kvq_equiv_bits(stack.model)}
+        log(f"[bench] formats {name}: {ms:.4f} ms/step, {res[name]['tokens_per_s']:.0f} tok/s, "
+            f"decode {res[name]['decode_gbps']:.0f} GB/s, {kv / 2**20:.0f} MiB/step")
+        del g, g_attn, stack
+        torch.cuda.empty_cache()
+    base = res["BF16"]["tokens_per_s"]
+    for r in res.values():
+        r["relative_to_BF16"] = r["tokens_per_s"] / base
+    mix = res["BF16/FP8 mix"]
+    rec = {"metric": "decode step tokens/s of the 8 BF16 + 24 FP8 layer mix (llama3.1-8b shape, B=16, 4096 cached "
+                     "tokens), 1 GPU",
+           "value": mix["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": mix["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16-in/fp32-acc, fp8 e4m3 + bf16 pages", "data": "synthetic",
+           "config": {"workload": CONFIGS["formats"]["workload"], "tables": list(FORMAT_TABLES)},
+           "formats": res, "roofline": None, "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
 

@@ -94,7 +94,7 @@ SWEEP_SHAPES = [(64, 128), (16, 512), (8, 1024), (16, 4096)]
 # sources the decode kernel is built from: a stored HBM-traffic measurement is reported only
 # while they are unchanged
 DECODE_SOURCES = ["layer_wise_mixed_kvq_amd/csrc/kvq_decode.hip", "layer_wise_mixed_kvq_amd/csrc/kvq_device.h",
-                  "layer_wise_mixed_kvq_amd/csrc/kvq_internal.h"]
+                  "layer_wise_mixed_kvq_amd/csrc/kvq_internal.h", "layer_wise_mixed_kvq_amd/csrc/kvq_codec.h"]
 COPY_BYTES = 1 << 30
 
 

@@ -558,6 +558,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     float *lse_bh = p.lse ? p.lse + bh * G : nullptr;
     const bool append = p.pos != nullptr;      // fused append: attend over pos + 1 tokens
     const int L = append ? p.pos[b] + 1 : p.seq_len[b];
+    // ---- requests that do not depend on the length, issued before it arrives: this wave's
+    // block-table ids (every page the split could hold), q, and the wave's first page (its
+    // id checked against the pool; unused if the sequence turns out shorter) -------------
+    const int wave = tid >> 6, lane = tid & 63;
+    const int P = p.pages_per_split;
+    const int pg_begin = split * P + wave;
+    const int pg_lim = min(p.max_pages, (split + 1) * P);
+    int my_phys = 0;
+    if (pg_begin + kWaves * lane < pg_lim)
+        my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + pg_begin + kWaves * lane];
+    // (unconditional loads at a clamped index: nothing waits on them until q is staged)
+    constexpr int kQPer = (HS * kHeadDim + kThreads - 1) / kThreads;
+    float qv[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+        const int i = tid + k * kThreads;
+        qv[k] = load_q<QT>(p.q, bh * G * kHeadDim + (i < G * kHeadDim ? i : 0));
+    }
 
     const bool bad_len = (append ? L <= 0 : L < 0) || L > p.max_seq_len || L > kGroup * p.max_pages;
     if (bad_len || L == 0) {
@@ -573,7 +591,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const bool flush = append && L % kGroup == 0;
     const int full = L / kGroup - (flush ? 1 : 0);      // pages read from the pool
     const int nres = flush ? kGroup : L % kGroup;       // tokens attended from the residual tile
-    const int P = p.pages_per_split;
     const int n_ps = (full + P - 1) / P;               // splits with pages
     const int n_work = n_ps > 0 ? n_ps : 1;             // workgroups of this (sequence, KV head)
     if (split >= n_work) return;
@@ -581,23 +598,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     // work while the last ones are still starting
     const bool has_res = nres > 0 && split == 0;
 
-    const int wave = tid >> 6, lane = tid & 63;
-    // ---- prologue: q, this wave's block-table ids and its first page are all requested
-    // before anything waits on them ------------------------------------------------------
-    constexpr int kQPer = (HS * kHeadDim + kThreads - 1) / kThreads;
-    float qv[kQPer];
+    const int pg_end = min(full, (split + 1) * P);
+    const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
+    // q arrives with the block-table ids: stage it before the page and residual requests so
+    // that nothing waits on those until the page loop
 #pragma unroll
     for (int k = 0; k < kQPer; ++k) {
         const int i = tid + k * kThreads;
-        qv[k] = i < G * kHeadDim ? load_q<QT>(p.q, bh * G * kHeadDim + i) * kScoreScale : 0.0f;
+        if (i < G * kHeadDim) sm.qs[i / kHeadDim][i % kHeadDim] = qv[k] * kScoreScale;
     }
-    const int pg_begin = split * P + wave;
-    const int pg_end = min(full, (split + 1) * P);
-    const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
-    int my_phys = 0;
-    if (lane < n_my) my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + pg_begin + kWaves * lane];
-    uint4 res_kv[4];
-    if (has_res) load_residual(p, bh, nres, append, res_kv);
     // lane roles in the page loop
     const int a = lane >> 4, r16 = lane & 15;
     const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
@@ -620,11 +629,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     };
     PageRegs<KB, VB> cur, nxt;
     if (n_my > 0) load_page<KB, VB, KM>(cur, page_base(0), lane, ch0, ch1, t0, t1);
-#pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-        const int i = tid + k * kThreads;
-        if (i < G * kHeadDim) sm.qs[i / kHeadDim][i % kHeadDim] = qv[k];
-    }
+    uint4 res_kv[4];
+    if (has_res) load_residual(p, bh, nres, append, res_kv);
     __syncthreads();
     // per-head normalization exponent: |q * 2^eq| in [1, 2); wave w reduces heads w, w+4, ...
     for (int hh = wave; hh < G; hh += kWaves) {

@@ -225,8 +225,8 @@ __device__ __forceinline__ uint32_t fp16x2_1024()
 template <int BITS>
 __device__ __forceinline__ constexpr int unpack_shift(int j)
 {
-    if constexpr (BITS > 8)
-        return 0;     // not a code width (floating-point layers)
+    if constexpr (BITS != 8)
+        return 0;     // 2- and 4-bit codes unpack exactly (below); not a code width (float layers)
     else
         return BITS * (j % (8 / BITS));
 }
@@ -249,13 +249,77 @@ __device__ __forceinline__ uint4 unpack_codes(const uint32_t *w, int op, uint32_
     return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-// Channel (within a lane's 32-channel k-group) of the low half of pair j of key operand jj.
+// 2- and 4-bit codes through the hardware's small-float conversions.  A 4-bit code alone
+// in a byte is the E4M3 value c * 2^-9 (subnormal below 8, normal from 8), and a 2-bit code
+// alone in a nibble is the E2M1 value c / 2; a power-of-two scale of 2^9 or 2 turns either
+// back into the integer c exactly (a normal fp16 value, or 0).  Two masks per word leave
+// one code per byte (or nibble), and each conversion yields one fp16 pair.
+//   4-bit, operand op = word op:    pairs (c0, c2), (c1, c3), (c4, c6), (c5, c7)
+//   2-bit, operand op = word op/2, bytes b = op%2 and b + 2 of its two masked copies:
+//                                   pairs (c[4b], c[4b+2]), (c[4b+1], c[4b+3]), then b + 2
+// where c[i] is the code at bit BITS*i of the word.
+template <int BITS>
+__device__ __forceinline__ uint4 unpack_cvt(const uint32_t *w, int op)
+{
+    half2_t r[4];
+    if constexpr (BITS == 4) {
+        const uint32_t x = w[op];
+        const uint32_t m0 = x & 0x0F0F0F0Fu, m1 = (x >> 4) & 0x0F0F0F0Fu;
+        r[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m0, 512.0f, false);
+        r[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m1, 512.0f, false);
+        r[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m0, 512.0f, true);
+        r[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m1, 512.0f, true);
+    } else {
+        static_assert(BITS == 2, "2- or 4-bit codes");
+        const uint32_t x = w[op >> 1];
+        const uint32_t m0 = x & 0x33333333u, m1 = (x >> 2) & 0x33333333u;
+        if (op & 1) {
+            r[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m0, 2.0f, 1);
+            r[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m1, 2.0f, 1);
+            r[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m0, 2.0f, 3);
+            r[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m1, 2.0f, 3);
+        } else {
+            r[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m0, 2.0f, 0);
+            r[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m1, 2.0f, 0);
+            r[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m0, 2.0f, 2);
+            r[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m1, 2.0f, 2);
+        }
+    }
+    return make_uint4(__builtin_bit_cast(uint32_t, r[0]), __builtin_bit_cast(uint32_t, r[1]),
+                      __builtin_bit_cast(uint32_t, r[2]), __builtin_bit_cast(uint32_t, r[3]));
+}
+
+// B operand `op` of a lane's packed codes: conversions for 2 and 4 bits, the 1024.0 insert
+// for 8 bits
+template <int BITS>
+__device__ __forceinline__ uint4 unpack_b(const uint32_t *w, int op, uint32_t magic)
+{
+    if constexpr (BITS == 8)
+        return unpack_codes<BITS>(w, op, magic);
+    else
+        return unpack_cvt<BITS>(w, op);
+}
+
+// Channel (within a lane's 32-channel k-group) of the first code of pair j of key operand
+// jj (per-channel keys); the second code is key_pair_step<KB>() channels further.
 template <int KB>
 __device__ __forceinline__ int key_pair_channel(int jj, int j)
 {
-    constexpr int n = 16 / KB, nd = 32 / KB;
-    const int k = 4 * jj + j;
-    return nd * (k / n) + (k % n);
+    if constexpr (KB == 4) {
+        return 8 * jj + 4 * (j >> 1) + (j & 1);
+    } else if constexpr (KB == 2) {
+        return 16 * (jj >> 1) + 4 * (jj & 1) + 8 * (j >> 1) + (j & 1);
+    } else {
+        constexpr int n = 16 / KB, nd = 32 / KB;
+        const int k = 4 * jj + j;
+        return nd * (k / n) + (k % n);
+    }
+}
+
+template <int KB>
+__device__ __forceinline__ constexpr int key_pair_step()
+{
+    return KB == 8 ? 16 / KB : 2;
 }
 
 // A-operand parts: fp16 hi | lo, or bf16 hi | mid | lo for BF16 layers
@@ -613,9 +677,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     // per-channel keys: any channel pair of the lane's 32-channel group; per-token keys: the
     // pair 32*kjj + 8*kq + 2*kj, + 1, so that matrix-core block kjj is exactly key group kjj
     // floating-point layers: the natural pair 2*lane, 2*lane + 1
-    const int ch0 = FLT ? 2 * lane : KT ? 32 * kjj + 8 * kq + 2 * kj : 32 * kq + key_pair_channel<KB>(kjj, kj);
-    const int ch1 = FLT || KT ? ch0 + 1 : ch0 + 16 / KB;
-    const int t0 = 8 * (r16 >> 2) + (r16 & 3), t1 = t0 + 4;   // value pair this lane folds (group a)
+    // (per-token keys with 2- or 4-bit codes: the pair holds slots 4 apart in one half-word,
+    // channels 32*kjj + 8*kq + 2*(kj%2) + kj/2 and 4 further)
+    const int ch0 = FLT                 ? 2 * lane
+                    : KT && KB == 8     ? 32 * kjj + 8 * kq + 2 * kj
+                    : KT                ? 32 * kjj + 8 * kq + 2 * (kj & 1) + (kj >> 1)
+                                        : 32 * kq + key_pair_channel<KB>(kjj, kj);
+    const int ch1 = FLT || (KT && KB == 8) ? ch0 + 1 : KT ? ch0 + 4 : ch0 + key_pair_step<KB>();
+    // value pair this lane folds (group a): tokens (w, w+4) of its octet for 8-bit codes,
+    // (w%2 + 4*(w/2), +2) for 2- and 4-bit codes, w = r16 % 4 -- the order their B operand
+    // pairs take
+    const int vw = r16 & 3;
+    const int t0 = 8 * (r16 >> 2) + (VB == 8 ? vw : (vw & 1) + 4 * (vw >> 1));
+    const int t1 = t0 + (VB == 8 ? 4 : 2);
     // powers of two the code unpack leaves on this lane's key channels / value tokens
     const int kshift = unpack_shift<KB>(kj), vshift = unpack_shift<VB>(r16 & 3);
     const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
@@ -806,7 +880,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 const uint4 alo = lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
-                    const uint4 bk = unpack_codes<KB>(cur.kc[blk], jj, magic);
+                    const uint4 bk = unpack_b<KB>(cur.kc[blk], jj, magic);
                     sacc[blk] = mfma(ahi, bk, jj == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : sacc[blk]);
                     sacc[blk] = mfma(alo, bk, sacc[blk]);
                 }
@@ -828,7 +902,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 const uint4 alo = lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
-                    const uint4 bk = unpack_codes<KB>(cur.kc[blk], jj, magic);
+                    const uint4 bk = unpack_b<KB>(cur.kc[blk], jj, magic);
                     sk[jj][blk] = mfma(alo, bk, mfma(ahi, bk, float4_t{0.f, 0.f, 0.f, 0.f}));
                 }
             }
@@ -956,7 +1030,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 const uint4 alo = lds_read16(&W.pp[1][g][arow][4 * a]);
 #pragma unroll
                 for (int nb = 2 * g; nb < 2 * g + 2; ++nb) {
-                    const uint4 bv = unpack_codes<VB>(cur.vc, nb, magic);
+                    const uint4 bv = unpack_b<VB>(cur.vc, nb, magic);
                     acc[nb] = mfma(ahi, bv, acc[nb]);
                     acc[nb] = mfma(alo, bv, acc[nb]);
                 }

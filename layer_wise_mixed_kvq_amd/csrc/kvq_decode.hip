@@ -39,6 +39,8 @@
 // h / 4 of the accumulator: with G <= 4 every lane holds exactly one head per token.
 //   scores:  D[head][token]   = A(q s hi|lo, from LDS)    x B(key codes, token-major rows)
 //   values:  D[head][channel] = A(p s hi|lo, from LDS)    x B(value codes, chunk layout)
+// With G <= 8 the hi and lo parts occupy different rows of one A operand (parts x head
+// slots <= 16), so one MFMA per B operand forms both and the parts are summed afterwards.
 //
 // Floating-point layers (FP8 E4M3 with one K and one V scale per KV head, or BF16) hold
 // the values themselves, so nothing is folded per page: the scales multiply the scores
@@ -729,7 +731,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             if (lane < 16 * PG) W.pp[part][lane / 16][HS][lane % 16] = 0u;
         }
         const int hr = 4 * (r16 & 3) + (r16 >> 2);             // head of A row r16
-        const int arow = hr < G ? hr : HS;                      // zero row when absent
+        // With few head slots the A-operand parts (hi / lo, or hi / mid / lo) share one
+        // matrix: part p of head slot hh is row slot p*HS + hh, so one MFMA forms every part
+        // and D element p*GS + i holds part p of head 4i + a (summed after the MFMA).
+        constexpr bool RS = NP * HS <= 16;
+        const int arow = RS ? ((hr < NP * HS && hr % HS < G) ? hr % HS : HS) : (hr < G ? hr : HS);
+        const int apart = RS && hr < NP * HS ? hr / HS : 0;
+        // element i of an MFMA result with its parts summed
+        auto dsum = [&](const float4_t &v, int i) -> float {
+            float x = v[i];
+            if constexpr (RS) {
+#pragma unroll
+                for (int part = 1; part < NP; ++part) x += v[part * GS + i];
+            }
+            return x;
+        };
         float qw[HS][2];                                        // q~ of the folded key pair, every head
         float qb[GS][8];                                        // q~ of the zero-term channels
         float inv_eq[GS];                                       // 2^-eq of the lane's heads
@@ -817,20 +833,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             for (int jj = 0; jj < 4; ++jj) {
                 uint4 av[NP];
 #pragma unroll
-                for (int part = 0; part < NP; ++part) av[part] = lds_read16(&W.qp[part][arow][16 * a + 4 * jj]);
+                for (int part = 0; part < (RS ? 1 : NP); ++part)
+                    av[part] = lds_read16(&W.qp[RS ? apart : part][arow][16 * a + 4 * jj]);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
                     float4_t c = jj == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : sacc[blk];
                     if constexpr (KM == kLayerFp8) {
                         const uint4 bk = fp8x8_to_f16(cur.kc[blk][2 * jj], cur.kc[blk][2 * jj + 1]);
-                        c = mfma(av[0], bk, c);
-                        c = mfma(av[1], bk, c);
+#pragma unroll
+                        for (int part = 0; part < (RS ? 1 : NP); ++part) c = mfma(av[part], bk, c);
                     } else {
                         const uint4 bk = make_uint4(cur.kc[blk][4 * jj], cur.kc[blk][4 * jj + 1], cur.kc[blk][4 * jj + 2],
                                                     cur.kc[blk][4 * jj + 3]);
-                        c = mfma_bf16(av[0], bk, c);
-                        c = mfma_bf16(av[1], bk, c);
-                        c = mfma_bf16(av[2], bk, c);
+#pragma unroll
+                        for (int part = 0; part < (RS ? 1 : NP); ++part) c = mfma_bf16(av[part], bk, c);
                     }
                     sacc[blk] = c;
                 }
@@ -838,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 0; i < GS; ++i)
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = sacc[blk][i] * ksc[i];
+                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = dsum(sacc[blk], i) * ksc[i];
           } else if constexpr (!KT) {
             // ---- page exponent: |q~ s 2^E| < 2^15 for every channel ---------------
             uint32_t smax = 0;
@@ -876,13 +892,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             float4_t sacc[2];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const uint4 ahi = lds_read16(&W.qp[0][arow][16 * a + 4 * jj]);
-                const uint4 alo = lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
+                const uint4 ahi = lds_read16(&W.qp[RS ? apart : 0][arow][16 * a + 4 * jj]);
+                const uint4 alo = RS ? ahi : lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
                     const uint4 bk = unpack_b<KB>(cur.kc[blk], jj, magic);
                     sacc[blk] = mfma(ahi, bk, jj == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : sacc[blk]);
-                    sacc[blk] = mfma(alo, bk, sacc[blk]);
+                    if constexpr (!RS) sacc[blk] = mfma(alo, bk, sacc[blk]);
                 }
             }
             const float sce = ldexpf(1.0f, -E);
@@ -891,19 +907,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 const float sc = sce * inv_eq[i];
                 const float bc = bias[i] * inv_eq[i];
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = fmaf(sacc[blk][i], sc, bc);
+                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = fmaf(dsum(sacc[blk], i), sc, bc);
             }
           } else {
             // ---- per-token keys: one accumulator per key group, then the token's scales --
             float4_t sk[4][2];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const uint4 ahi = lds_read16(&W.qp[0][arow][16 * a + 4 * jj]);
-                const uint4 alo = lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
+                const uint4 ahi = lds_read16(&W.qp[RS ? apart : 0][arow][16 * a + 4 * jj]);
+                const uint4 alo = RS ? ahi : lds_read16(&W.qp[1][arow][16 * a + 4 * jj]);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
                     const uint4 bk = unpack_b<KB>(cur.kc[blk], jj, magic);
-                    sk[jj][blk] = mfma(alo, bk, mfma(ahi, bk, float4_t{0.f, 0.f, 0.f, 0.f}));
+                    sk[jj][blk] = mfma(ahi, bk, float4_t{0.f, 0.f, 0.f, 0.f});
+                    if constexpr (!RS) sk[jj][blk] = mfma(alo, bk, sk[jj][blk]);
                 }
             }
 #pragma unroll
@@ -914,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const uint32_t w = cur.kszb[4 * blk + jj];
-                        raw = fmaf(half_bits_to_float(w & 0xFFFFu), sk[jj][blk][i], raw);
+                        raw = fmaf(half_bits_to_float(w & 0xFFFFu), dsum(sk[jj][blk], i), raw);
                         raw = fmaf(half_bits_to_float(w >> 16), qsum[i][jj], raw);
                     }
                     s2[blk][i] = raw * inv_eq[i];
@@ -938,7 +955,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     m_run[i] = mn;
                     l_part[i] *= alpha[i];
 #pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) acc[nb][i] *= alpha[i];
+                    for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+                        for (int part = 0; part < (RS ? NP : 1); ++part) acc[nb][part * GS + i] *= alpha[i];
+                    }
                     if (!FLT && r16 == 0) W.alpha[4 * i + a] = alpha[i];
                 }
                 if constexpr (!FLT) {
@@ -975,18 +995,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             wave_lds_sync();
             uint4 av[NP];
 #pragma unroll
-            for (int part = 0; part < NP; ++part) av[part] = lds_read16(&W.pp[part][0][arow][4 * a]);
+            for (int part = 0; part < (RS ? 1 : NP); ++part) av[part] = lds_read16(&W.pp[RS ? apart : part][0][arow][4 * a]);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 if constexpr (KM == kLayerFp8) {
                     const uint4 bv = fp8x8_to_f16(cur.vc[2 * nb], cur.vc[2 * nb + 1]);
-                    acc[nb] = mfma(av[0], bv, acc[nb]);
-                    acc[nb] = mfma(av[1], bv, acc[nb]);
+#pragma unroll
+                    for (int part = 0; part < (RS ? 1 : NP); ++part) acc[nb] = mfma(av[part], bv, acc[nb]);
                 } else {
                     const uint4 bv = make_uint4(cur.vc[4 * nb], cur.vc[4 * nb + 1], cur.vc[4 * nb + 2], cur.vc[4 * nb + 3]);
-                    acc[nb] = mfma_bf16(av[0], bv, acc[nb]);
-                    acc[nb] = mfma_bf16(av[1], bv, acc[nb]);
-                    acc[nb] = mfma_bf16(av[2], bv, acc[nb]);
+#pragma unroll
+                    for (int part = 0; part < (RS ? 1 : NP); ++part) acc[nb] = mfma_bf16(av[part], bv, acc[nb]);
                 }
             }
           } else {
@@ -1026,13 +1045,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             // ---- values on MFMA ------------------------------------------------------
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint4 ahi = lds_read16(&W.pp[0][g][arow][4 * a]);
-                const uint4 alo = lds_read16(&W.pp[1][g][arow][4 * a]);
+                const uint4 ahi = lds_read16(&W.pp[RS ? apart : 0][g][arow][4 * a]);
+                const uint4 alo = RS ? ahi : lds_read16(&W.pp[1][g][arow][4 * a]);
 #pragma unroll
                 for (int nb = 2 * g; nb < 2 * g + 2; ++nb) {
                     const uint4 bv = unpack_b<VB>(cur.vc, nb, magic);
                     acc[nb] = mfma(ahi, bv, acc[nb]);
-                    acc[nb] = mfma(alo, bv, acc[nb]);
+                    if constexpr (!RS) acc[nb] = mfma(alo, bv, acc[nb]);
                 }
             }
           }
@@ -1071,13 +1090,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-                for (int i = 0; i < GS; ++i) o_out[nb][i] = acc[nb][i] * unscale;
+                for (int i = 0; i < GS; ++i) o_out[nb][i] = dsum(acc[nb], i) * unscale;
         } else {
             const float unscale = ldexpf(1.0f, -ev);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-                for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(acc[nb][i], unscale, W.bv[nb >> 1][4 * i + a]);
+                for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(dsum(acc[nb], i), unscale, W.bv[nb >> 1][4 * i + a]);
         }
         __syncthreads();     // every wave is done with its WaveLds: reuse the space
         if (has_res) bad_page |= !residual_tokens<KB, VB, GS, KM>(p, sm, res_kv, nres, G, bh, append, flush, full);

@@ -1124,32 +1124,43 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         const MergeLds<GS> &M = sm.u.merge;
         float *part_o = p.part_o + (slot0 + split) * G * kHeadDim;
         float *part_ml = p.part_ml + (slot0 + split) * G * 2;
-        for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
-            const int hh = idx / kHeadDim, c = idx % kHeadDim;
+        // one thread per 4 consecutive channels of a head: the head's weights once, then
+        // 16-byte reads of the waves' partial outputs (exponents <= 0: the raw exp2)
+        constexpr int kVec = 4, kPerHead = kHeadDim / kVec;
+        for (int it = tid; it < G * kPerHead; it += kThreads) {
+            const int hh = it / kPerHead, c = (it % kPerHead) * kVec, idx = hh * kHeadDim + c;
             float m = has_res ? sm.ro.m[hh] : -INFINITY;
             if (n_ps > 0) {
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) m = fmaxf(m, M.m[w][hh]);
             }
-            float l = 0.0f, o = 0.0f;
+            float l = 0.0f;
+            float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (has_res) {
-                const float wt = exp2f(sm.ro.m[hh] - m);
+                const float wt = __builtin_amdgcn_exp2f(sm.ro.m[hh] - m);
+                const float4 r = *reinterpret_cast<const float4 *>(&sm.ro.o[hh][c]);
                 l = wt * sm.ro.l[hh];
-                o = wt * sm.ro.o[hh][c];
+                o = make_float4(wt * r.x, wt * r.y, wt * r.z, wt * r.w);
             }
             if (n_ps > 0) {
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) {
-                    const float wt = M.m[w][hh] == -INFINITY ? 0.0f : exp2f(M.m[w][hh] - m);
+                    const float wt = M.m[w][hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M.m[w][hh] - m);
+                    const float4 r = *reinterpret_cast<const float4 *>(&M.o[w][hh][c]);
                     l = fmaf(wt, M.l[w][hh], l);
-                    o = fmaf(wt, M.o[w][hh][c], o);
+                    o = make_float4(fmaf(wt, r.x, o.x), fmaf(wt, r.y, o.y), fmaf(wt, r.z, o.z), fmaf(wt, r.w, o.w));
                 }
             }
             if (single) {
-                out_bh[idx] = bad ? NAN : o / l;
+                const float inv = 1.0f / l;
+                *reinterpret_cast<float4 *>(&out_bh[idx]) =
+                    bad ? make_float4(NAN, NAN, NAN, NAN) : make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
                 if (lse_bh && c == 0) lse_bh[hh] = bad ? NAN : (m + log2f(l)) * kLn2;
             } else {
-                store_dev(&part_o[idx], bad ? NAN : o);
+                store_dev(&part_o[idx], bad ? NAN : o.x);
+                store_dev(&part_o[idx + 1], bad ? NAN : o.y);
+                store_dev(&part_o[idx + 2], bad ? NAN : o.z);
+                store_dev(&part_o[idx + 3], bad ? NAN : o.w);
                 if (c == 0) {
                     store_dev(&part_ml[2 * hh], bad ? 0.0f : m);
                     store_dev(&part_ml[2 * hh + 1], bad ? NAN : l);
@@ -1224,7 +1235,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             if (idx < G * kHeadDim)
                 for (int s2 = 0; s2 < cnt; ++s2) mc = fmaxf(mc, C.m[s2][g]);
             mn[it] = fmaxf(mx[it], mc);
-            const float sc = mx[it] == -INFINITY ? 0.0f : exp2f(mx[it] - mn[it]);
+            const float sc = mx[it] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mx[it] - mn[it]);
             ls[it] *= sc;
             os[it] *= sc;
             mx[it] = mn[it];
@@ -1239,7 +1250,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
                     for (int k = 0; k < kBatch; ++k) {
                         if (s0 + k < cnt) {
-                            const float w = exp2f(C.m[s0 + k][g] - mn[it]);
+                            const float w = __builtin_amdgcn_exp2f(C.m[s0 + k][g] - mn[it]);
                             ls[it] = fmaf(w, C.l[s0 + k][g], ls[it]);
                             os[it] = fmaf(w, x[it][k], os[it]);
                         }

@@ -188,27 +188,23 @@ constexpr int layer_page_bytes()
 
 // E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; no infinities; S.1111.111
 // is NaN; largest finite 448.  Round to nearest even; finite values beyond 448 saturate.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x)
+// The hardware conversion (v_cvt_scalef32_pk_fp8_f32, scale 1) of the value clamped to
+// [-448, 448] is exactly that rule -- checked against a direct implementation of the
+// definition on every E4M3 value, every tie between neighbours, the saturation boundary,
+// signed zeros and millions of random inputs -- so only NaN needs its own code.  Two
+// values per call, as bytes 0 and 1 of the result.
+typedef short kvq_short2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b)
 {
-    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-    const float a = fabsf(x);
-    if (a == 0.0f) return sign;
-    if (a != a) return sign | 0x7Fu;
-    if (a > 3.0e38f) return sign | 0x7Eu;
-    int e;
-    frexpf(a, &e);
-    int E = e - 1;
-    if (E < -6) E = -6;                                   // subnormal spacing 2^-9
-    float n = __builtin_rintf(ldexpf(a, 3 - E));          // exact scaling, then ties to even
-    if (n == 0.0f) return sign;
-    if (n >= 16.0f) {
-        n *= 0.5f;
-        E += 1;
-    }
-    if (E > 8 || (E == 8 && n > 14.0f)) return sign | 0x7Eu;
-    const uint32_t ni = static_cast<uint32_t>(n);
-    if (ni < 8u) return sign | ni;
-    return sign | (static_cast<uint32_t>(E + 7) << 3) | (ni - 8u);
+    const kvq_short2 zero = {0, 0};
+    const uint32_t w = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero, fminf(fmaxf(a, -448.0f), 448.0f),
+                                                           fminf(fmaxf(b, -448.0f), 448.0f), 1.0f, false));
+    uint32_t lo = w & 0xFFu, hi = (w >> 8) & 0xFFu;
+    if (a != a) lo = ((__float_as_uint(a) >> 24) & 0x80u) | 0x7Fu;
+    if (b != b) hi = ((__float_as_uint(b) >> 24) & 0x80u) | 0x7Fu;
+    return lo | (hi << 8);
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
@@ -237,14 +233,17 @@ __device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, fl
         {
             const int t = d / (kHeadDim / kPer), c0 = (d % (kHeadDim / kPer)) * kPer;
             uint32_t w = 0;
+            if constexpr (FMT == kLayerFp8) {
+                float *x = &sm.k[t * kTileStride + c0];
+                w = e4m3_pair(x[0] / ks, x[1] / ks) | (e4m3_pair(x[2] / ks, x[3] / ks) << 16);
+                if constexpr (DEQUANT) {
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                float &x = sm.k[t * kTileStride + c0 + i];
-                if constexpr (FMT == kLayerFp8) {
-                    const uint32_t b = f32_to_e4m3(x / ks);
-                    w |= b << (8 * i);
-                    if constexpr (DEQUANT) x = e4m3_to_f32(b) * ks;
-                } else {
+                    for (int i = 0; i < kPer; ++i) x[i] = e4m3_to_f32((w >> (8 * i)) & 0xFFu) * ks;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    float &x = sm.k[t * kTileStride + c0 + i];
                     const uint32_t b = float_to_bf16_bits(x);
                     w |= b << (16 * i);
                     if constexpr (DEQUANT) x = bf16_bits_to_float(static_cast<uint16_t>(b));
@@ -256,14 +255,18 @@ __device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, fl
         {
             const int c = d / (kGroup / kPer), t0 = (d % (kGroup / kPer)) * kPer;
             uint32_t w = 0;
+            if constexpr (FMT == kLayerFp8) {
+                float *x0 = &sm.v[t0 * kTileStride + c];
+                w = e4m3_pair(x0[0] / vs, x0[kTileStride] / vs) |
+                    (e4m3_pair(x0[2 * kTileStride] / vs, x0[3 * kTileStride] / vs) << 16);
+                if constexpr (DEQUANT) {
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                float &x = sm.v[(t0 + i) * kTileStride + c];
-                if constexpr (FMT == kLayerFp8) {
-                    const uint32_t b = f32_to_e4m3(x / vs);
-                    w |= b << (8 * i);
-                    if constexpr (DEQUANT) x = e4m3_to_f32(b) * vs;
-                } else {
+                    for (int i = 0; i < kPer; ++i) x0[i * kTileStride] = e4m3_to_f32((w >> (8 * i)) & 0xFFu) * vs;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    float &x = sm.v[(t0 + i) * kTileStride + c];
                     const uint32_t b = float_to_bf16_bits(x);
                     w |= b << (16 * i);
                     if constexpr (DEQUANT) x = bf16_bits_to_float(static_cast<uint16_t>(b));

@@ -334,7 +334,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama", choices=sorted(CONFIGS))
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
-    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=5, help="sequences in the CPU-baseline sample (0 = skip)")
     ap.add_argument("--roofline-reps", type=int, default=5)
     ap.add_argument("--unfused", action="store_true", help="append as its own launch before each attention launch")
     args = ap.parse_args()

@@ -7,6 +7,8 @@ even with saturation, computed from x / scale in binary32 on both sides); attent
 group sizes and split sizes; the fused append (including flushes) against the oracle and
 the two-launch path; a model that mixes integer, FP8 and BF16 layers.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -162,3 +164,38 @@ def test_mixed_integer_fp8_bf16_model(kvq, orc):
         assert np.array_equal(cache.pages.cpu().numpy(), c.o_pages), f"layer {l}: pages"
         o_ref, l_ref = c.oracle_decode(orc)
         assert_attention_close(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"layer {l}")
+
+
+def _e4m3_values_and_ties():
+    """Every finite E4M3 value, every midpoint between neighbours (exact ties), both signs,
+    plus signed zeros, tiny values and values past the largest finite 448."""
+    vals = []
+    for b in range(128):
+        e, m = (b >> 3) & 15, b & 7
+        if e == 15 and m == 7:
+            continue
+        v = math.ldexp(8 + m, e - 10) if e else math.ldexp(m, -9)
+        nxt = math.ldexp(16, e - 10) if m == 7 else (math.ldexp(9 + m, e - 10) if e else math.ldexp(m + 1, -9))
+        vals += [v, -v, (v + nxt) / 2, -(v + nxt) / 2]
+    vals += [0.0, -0.0, 1e-30, -1e-30, 448.5, 463.9, 464.0, 465.0, 480.0, 1e6, -1e6]
+    return np.array(vals, dtype=np.float32)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.03125, 0.7])
+def test_fp8_encode_every_value_and_tie(kvq, orc, scale):
+    """Pages of K and V tiles holding every E4M3 value and tie (times the scale) are
+    bit-exact with the oracle's encoder (round to nearest even, saturation at 448)."""
+    import torch
+    vals = _e4m3_values_and_ties() * np.float32(scale)
+    c = Case(8, 8, H=1, G=1, lens=[64], seed=11, kmode=FP8, scales=[[scale, scale]], src="f32")
+    k = c.k.clone()
+    v = c.v.clone()
+    flat = np.resize(vals, 64 * 128).reshape(1, 64, 1, 128)
+    k[:] = torch.from_numpy(flat)
+    v[:] = torch.from_numpy(np.ascontiguousarray(flat[:, ::-1]))
+    c.k, c.v = k, v
+    log(f"fp8 every value scale={scale}")
+    c.oracle_pack(orc)
+    c.device_setup(kvq)
+    c.device_pack(kvq)
+    assert np.array_equal(c.cache.pages.cpu().numpy(), c.o_pages)

@@ -228,3 +228,43 @@ def test_graph_replay_matches_eager(kvq, orc):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i} differs"
+
+
+def _tie_tile(bits, T, H, seed):
+    """fp32 source whose groups get min 0 and max (2^bits - 1) * S with S = 1434/2048 (an
+    fp16 value, so the stored scale is exactly S and the zero 0), every other value being
+    fl((k + 0.5) * S) moved by -2 .. +2 ulps: quotients at and beside half-integers, where
+    any departure from one correctly rounded binary32 division changes the code."""
+    L = (1 << bits) - 1
+    S = np.float32(1434.0 / 2048.0)
+    rng = np.random.default_rng(seed)
+    x = ((rng.integers(0, L, (1, T, H, 128)).astype(np.float32) + np.float32(0.5)) * S).astype(np.float32)
+    steps = rng.integers(-2, 3, x.shape)
+    for _ in range(2):
+        x = np.where(steps > 0, np.nextafter(x, np.float32(np.inf)), np.where(steps < 0, np.nextafter(x, np.float32(0)), x))
+        steps = steps - np.sign(steps)
+    return x.astype(np.float32), np.float32(L) * S
+
+
+@pytest.mark.parametrize("kb,vb,kmode", [(2, 2, 0), (4, 4, 0), (8, 8, 0), (4, 2, 0), (4, 4, 1), (2, 8, 1)])
+def test_pack_rounding_ties_bit_exact(kvq, orc, kb, vb, kmode):
+    """Quotients at and beside half-integers (rounding ties of the code rule) pack
+    bit-exactly as the oracle does, in both key modes."""
+    import torch
+    T, H = 64, 2
+    c = Case(kb, vb, H=H, G=1, lens=[T], seed=kb * 7 + vb + kmode, src="f32", kmode=kmode)
+    kt, Lk = _tie_tile(kb, T, H, 1 + kb)
+    vt, Lv = _tie_tile(vb, T, H, 2 + vb)
+    # group extremes: per-channel keys over each page's 32 tokens, per-token groups over
+    # 32 channels (values, and keys in the per-token mode)
+    if kmode == 0:
+        kt[:, 0::32], kt[:, 1::32] = 0.0, Lk
+    else:
+        kt[..., 0::32], kt[..., 1::32] = 0.0, Lk
+    vt[..., 0::32], vt[..., 1::32] = 0.0, Lv
+    c.k, c.v = torch.from_numpy(kt), torch.from_numpy(vt)
+    log(f"rounding ties kb={kb} vb={vb} kmode={kmode}")
+    c.oracle_pack(orc)
+    c.device_setup(kvq)
+    c.device_pack(kvq)
+    assert np.array_equal(c.cache.pages.cpu().numpy(), c.o_pages)

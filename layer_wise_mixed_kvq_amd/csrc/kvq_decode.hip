@@ -14,12 +14,14 @@
 // the raw integer codes:
 //   score(t) = sum_c q_c (k_tc s_c + z_c) = sum_c (q_c s_c) k_tc + sum_c q_c z_c
 //   out(c)   = sum_t p_t (v_tc s_tg + z_tg) = sum_t (p_t s_tg) v_tc + sum_t p_t z_tg
-// Codes are unpacked with a shift, a bit-insert into 1024.0 and a packed subtract per pair
-// into exact normal fp16 integers: the matrix cores accumulate subnormal fp16 operands
+// Codes are unpacked into exact normal fp16 integers: 2- and 4-bit codes by the FP4 / FP8
+// conversion instructions (one instruction per pair), 8-bit codes by a bit-insert into
+// 1024.0 and a packed subtract.  The matrix cores accumulate subnormal fp16 operands
 // several bits less accurately, which the scores (a small difference of two large sums)
 // and the value sums do not tolerate.  The folded operands (q s and p s) are split into
-// fp16 hi + lo parts (22 significant bits) and both parts are fed to the MFMA with the same
-// code operand.  Both are scaled by powers of two so their largest values sit just below
+// fp16 hi + lo parts (22 significant bits) and both parts meet the same code operand (in
+// one MFMA, as different rows, when the head slots leave room).  Both are scaled by powers
+// of two so their largest values sit just below
 // 2^15: q s per page (from the page's largest key scale), p s per wave (from the largest
 // value scale seen so far, p <= 1).  That keeps the lo parts in the normal fp16 range, where
 // the matrix cores accumulate at full binary32 accuracy.
@@ -27,9 +29,9 @@
 // Work decomposition.  One workgroup of four waves per (split, KV head, sequence).  Split
 // s covers pages [s*P, min((s+1)*P, full)), each wave taking every fourth page.  A wave
 // keeps its own online-softmax state; the four are merged in LDS, and every split writes
-// (m, l, o[128]) per query head to the workspace.  The last split of a (sequence, KV head)
-// to finish -- a device-scope counter -- attends over the L mod 32 bf16 residual tokens
-// itself and merges everything:
+// (m, l, o[128]) per query head to the workspace.  Split 0 also attends over the residual
+// tokens (read into registers at kernel start).  The last split of a (sequence, KV head)
+// to finish -- a device-scope counter -- merges everything:
 //   m = max m_s, l = sum 2^(m_s - m) l_s, out = sum 2^(m_s - m) o_s / l, lse = (m + log2 l) ln 2
 // and resets the counter for the next call.  Scores are in log2 units (q carries
 // log2(e)/sqrt(128)).

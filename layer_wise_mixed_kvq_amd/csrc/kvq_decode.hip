@@ -402,6 +402,13 @@ __device__ __forceinline__ float load_dev(const float *p)
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Position of channel c inside a head's 128 split-partial outputs: (c % 4) * 32 + c / 4,
+// so that a thread's 4 consecutive channels go out as 4 stores of consecutive addresses.
+__device__ __forceinline__ int part_slot(int c)
+{
+    return (c % 4) * (kHeadDim / 4) + c / 4;
+}
+
 __device__ __forceinline__ void wait_stores()
 {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1159,10 +1166,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     bad ? make_float4(NAN, NAN, NAN, NAN) : make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
                 if (lse_bh && c == 0) lse_bh[hh] = bad ? NAN : (m + log2f(l)) * kLn2;
             } else {
-                store_dev(&part_o[idx], bad ? NAN : o.x);
-                store_dev(&part_o[idx + 1], bad ? NAN : o.y);
-                store_dev(&part_o[idx + 2], bad ? NAN : o.z);
-                store_dev(&part_o[idx + 3], bad ? NAN : o.w);
+                float *po = part_o + hh * kHeadDim;
+                store_dev(po + part_slot(c), bad ? NAN : o.x);
+                store_dev(po + part_slot(c + 1), bad ? NAN : o.y);
+                store_dev(po + part_slot(c + 2), bad ? NAN : o.z);
+                store_dev(po + part_slot(c + 3), bad ? NAN : o.w);
                 if (c == 0) {
                     store_dev(&part_ml[2 * hh], bad ? 0.0f : m);
                     store_dev(&part_ml[2 * hh + 1], bad ? NAN : l);
@@ -1204,7 +1212,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
                 for (int k = 0; k < kBatch; ++k)
                     x[it][k] = (idx < G * kHeadDim && s0 + k < cnt)
-                                   ? load_dev(p.part_o + ((slot0 + c0 + s0 + k) * G + g) * kHeadDim + c)
+                                   ? load_dev(p.part_o + ((slot0 + c0 + s0 + k) * G + g) * kHeadDim + part_slot(c))
                                    : 0.0f;
             }
         };

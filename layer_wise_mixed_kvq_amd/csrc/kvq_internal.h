@@ -50,7 +50,7 @@ struct DecodeParams {
     const float *scales;         // FP8 layers: [H][2] K / V scale, or null (1.0)
     float *out;
     float *lse;
-    float *part_o;        // [batch][H][n_splits][G][128]
+    float *part_o;        // [batch][H][n_splits][G][128], channel c at (c % 4) * 32 + c / 4
     float *part_ml;       // [batch][H][n_splits][G][2]  (running max in log2 units, sum)
     int *counters;        // [batch][H]
     long long n_pages;

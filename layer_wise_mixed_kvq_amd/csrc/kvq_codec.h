@@ -47,12 +47,14 @@ __device__ __forceinline__ void quant_group(float *x, int stride, uint32_t &sz_w
     float mn, mx;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) v[i] = x[i * stride] + 0.0f;   // -0 -> +0
+    // the values are finite and -0 is gone, so the hardware min / max (v_min3 / v_max3
+    // after contraction) give exactly the comparison-based extremes
     mn = v[0];
     mx = v[0];
 #pragma unroll
     for (int i = 1; i < kGroup; ++i) {
-        mn = v[i] < mn ? v[i] : mn;
-        mx = v[i] > mx ? v[i] : mx;
+        mn = __builtin_fminf(mn, v[i]);
+        mx = __builtin_fmaxf(mx, v[i]);
     }
     constexpr float levels = static_cast<float>((1 << BITS) - 1);
     const float s32 = (mx - mn) / levels;
@@ -65,10 +67,8 @@ __device__ __forceinline__ void quant_group(float *x, int stride, uint32_t &sz_w
         uint32_t code = 0;
         if (s != 0.0f) {
             const float q = (v[i] - z) / s;
-            float r = __builtin_rintf(q);
-            r = r < 0.0f ? 0.0f : r;
-            r = r > levels ? levels : r;
-            code = static_cast<uint32_t>(r);
+            // round half to even, then clamp to [0, levels] (one v_med3_f32)
+            code = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(__builtin_rintf(q), 0.0f, levels));
         }
         codes[i * code_stride] = static_cast<uint8_t>(code);
         if constexpr (DEQUANT) x[i * stride] = __builtin_fmaf(static_cast<float>(code), s, z);

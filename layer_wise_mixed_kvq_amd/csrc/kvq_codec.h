@@ -1,6 +1,7 @@
 // kvq_codec.h -- the page codec shared by the quantize-on-write kernels (prefill pack,
 // append + flush) and by the decode kernel's fused append: one 32-token page of one KV
-// head, staged in LDS as binary32, quantized by one workgroup of 256 threads.
+// head, staged in LDS (as binary32, or as the bfloat16 values themselves), quantized by one
+// workgroup of 256 threads.
 //
 // Keys are quantized per channel over the page's 32 tokens, values per token over groups
 // of 32 channels, each group with an fp16 scale (max - min) / (2^bits - 1) and an fp16
@@ -26,31 +27,98 @@
 namespace kvq {
 
 constexpr int kCodecThreads = 256;
-constexpr int kTileStride = kHeadDim + 1;   // padded row: column walks hit distinct banks
 
-struct QuantSmem {
-    float k[kGroup * kTileStride];           // [token][channel], binary32
-    float v[kGroup * kTileStride];
+// Element type of a staged tile: binary32, or the bits of a bfloat16 source staged as they
+// are (every bfloat16 value is exactly a binary32 value, so the codec computes the same
+// thing from either; the bfloat16 tile takes half the LDS, so twice as many workgroups fit
+// on a CU).
+template <typename T>
+struct TileElem;
+
+template <>
+struct TileElem<float> {
+    static constexpr int kStride = kHeadDim + 1;   // padded row: column walks hit distinct banks
+    __device__ static float get(const float *p) { return *p; }
+};
+
+template <>
+struct TileElem<uint16_t> {
+    static constexpr int kStride = kHeadDim + 8;   // 272-byte rows: 16-byte aligned, 4 banks apart
+    __device__ static float get(const uint16_t *p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
+};
+
+template <typename T>
+struct QuantSmemT;
+
+// binary32 tiles: with DEQUANT they are rewritten after the codes, so the codes keep their
+// own space
+template <>
+struct QuantSmemT<float> {
+    static constexpr int kStride = TileElem<float>::kStride;
+    static constexpr bool kCodesOverTiles = false;
+    float k[kGroup * kStride];               // [token][channel]
+    float v[kGroup * kStride];
     uint8_t kcode[kGroup * kHeadDim];        // [token][channel]
     uint8_t vcode[kHeadDim * kGroup];        // [channel][token]
 };
 
-// Codec of one 32-value group held by one thread.  Strict IEEE binary32: the compiler
-// must not contract or reassociate anything in here.  With DEQUANT the group's values are
-// replaced by their dequantized values code * s + z (binary32, one rounding).
-template <int BITS, bool DEQUANT>
-__device__ __forceinline__ void quant_group(float *x, int stride, uint32_t &sz_word, uint8_t *codes,
-                                            int code_stride)
+// bfloat16 tiles: every thread reads its group into registers before any code is written
+// (a barrier apart), so the codes reuse the tiles' space
+template <>
+struct QuantSmemT<uint16_t> {
+    static constexpr int kStride = TileElem<uint16_t>::kStride;
+    static constexpr bool kCodesOverTiles = true;
+    union {
+        struct {
+            alignas(16) uint16_t k[kGroup * kStride];
+            alignas(16) uint16_t v[kGroup * kStride];
+        };
+        struct {
+            uint8_t kcode[kGroup * kHeadDim];
+            uint8_t vcode[kHeadDim * kGroup];
+        };
+    };
+};
+
+using QuantSmem = QuantSmemT<float>;
+constexpr int kTileStride = QuantSmem::kStride;
+
+// The 32 values of one group, `stride` elements apart, as binary32 (-0 becomes +0).
+template <typename T>
+__device__ __forceinline__ void load_group(const T *x, int stride, float (&v)[kGroup])
+{
+    if constexpr (sizeof(T) == 2) {
+        if (stride == 1) {   // a row segment: four 16-byte reads
+#pragma unroll
+            for (int q = 0; q < kGroup / 8; ++q) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(__builtin_assume_aligned(x + 8 * q, 16));
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[8 * q + 2 * e] = __uint_as_float(w[e] << 16) + 0.0f;
+                    v[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u) + 0.0f;
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) v[i] = TileElem<T>::get(x + i * stride) + 0.0f;
+}
+
+// Codec of one 32-value group held by one thread (its values v, read by load_group).
+// Strict IEEE binary32: the compiler must not contract or reassociate anything in here.
+// With DEQUANT the group's tile values x are replaced by their dequantized values
+// code * s + z (binary32, one rounding).
+template <int BITS, bool DEQUANT, typename T>
+__device__ __forceinline__ void encode_group(const float (&v)[kGroup], T *x, int stride, uint32_t &sz_word,
+                                             uint8_t *codes, int code_stride)
 {
 #pragma clang fp contract(off)
-    float v[kGroup];
-    float mn, mx;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) v[i] = x[i * stride] + 0.0f;   // -0 -> +0
+    static_assert(!DEQUANT || sizeof(T) == 4, "dequantized values are written back as binary32");
     // the values are finite and -0 is gone, so the hardware min / max (v_min3 / v_max3
     // after contraction) give exactly the comparison-based extremes
-    mn = v[0];
-    mx = v[0];
+    float mn = v[0], mx = v[0];
 #pragma unroll
     for (int i = 1; i < kGroup; ++i) {
         mn = __builtin_fminf(mn, v[i]);
@@ -92,29 +160,40 @@ __device__ __forceinline__ int ktok_slot_channel(int a, int slot)
 // Quantize the staged tiles of one page-head into `dst` (global).  All 256 threads of the
 // workgroup call it; with DEQUANT the tiles hold the dequantized values afterwards (valid
 // after the workgroup's next barrier).  KTOK selects the per-token key mode.
-template <int KB, int VB, bool DEQUANT = false, bool KTOK = false>
-__device__ void quantize_page(QuantSmem &sm, uint8_t *__restrict__ dst)
+template <int KB, int VB, bool DEQUANT = false, bool KTOK = false, typename T>
+__device__ void quantize_page(QuantSmemT<T> &sm, uint8_t *__restrict__ dst)
 {
     using P = PageLayout<KB, VB>;
+    constexpr int kTileStride = QuantSmemT<T>::kStride;
     const int tid = threadIdx.x;
     uint32_t *dst32 = reinterpret_cast<uint32_t *>(dst);
-    if (tid < kHeadDim) {
-        uint32_t w;
+    // the thread's group: threads 0..127 a key group (channel tid, or in the per-token mode
+    // token tid % 32 and channels 32 (tid / 32) ..), threads 128..255 the value group of
+    // token (tid - 128) % 32 and channels 32 ((tid - 128) / 32) ..
+    const bool is_k = tid < kHeadDim;
+    const int t = tid & (kGroup - 1), j = (tid & (kHeadDim - 1)) >> 5;
+    float v[kGroup];
+    if (is_k) {
+        if constexpr (KTOK)
+            load_group(&sm.k[t * kTileStride + kGroup * j], 1, v);
+        else
+            load_group(&sm.k[tid], kTileStride, v);
+    } else {
+        load_group(&sm.v[t * kTileStride + kGroup * j], 1, v);
+    }
+    if constexpr (QuantSmemT<T>::kCodesOverTiles) __syncthreads();   // the codes overwrite the tiles
+    uint32_t w;
+    if (is_k) {
         if constexpr (KTOK) {
-            const int t = tid & (kGroup - 1), j = tid >> 5;
-            quant_group<KB, DEQUANT>(&sm.k[t * kTileStride + kGroup * j], 1, w, &sm.kcode[t * kHeadDim + kGroup * j], 1);
+            encode_group<KB, DEQUANT>(v, &sm.k[t * kTileStride + kGroup * j], 1, w, &sm.kcode[t * kHeadDim + kGroup * j], 1);
             dst32[P::kKSz / 4 + kValueGroups * t + j] = w;
         } else {
-            const int c = tid;
-            quant_group<KB, DEQUANT>(&sm.k[c], kTileStride, w, &sm.kcode[c], kHeadDim);
-            dst32[P::kKSz / 4 + c] = w;
+            encode_group<KB, DEQUANT>(v, &sm.k[tid], kTileStride, w, &sm.kcode[tid], kHeadDim);
+            dst32[P::kKSz / 4 + tid] = w;
         }
     } else {
-        const int t = (tid - kHeadDim) & (kGroup - 1);
-        const int j = (tid - kHeadDim) >> 5;
-        uint32_t w;
-        quant_group<VB, DEQUANT>(&sm.v[t * kTileStride + kGroup * j], 1, w, &sm.vcode[(kGroup * j) * kGroup + t],
-                                 kGroup);
+        encode_group<VB, DEQUANT>(v, &sm.v[t * kTileStride + kGroup * j], 1, w, &sm.vcode[(kGroup * j) * kGroup + t],
+                                  kGroup);
         dst32[P::kVSz / 4 + kValueGroups * t + j] = w;
     }
     __syncthreads();
@@ -218,11 +297,14 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
 // threads call it; every output dword is built from tile elements no other thread reads,
 // so with DEQUANT the tiles are overwritten in place with the values the page stores
 // (E4M3 value * scale, binary32), valid after the workgroup's next barrier.
-template <int FMT, bool DEQUANT = false>
-__device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, float ks, float vs)
+template <int FMT, bool DEQUANT = false, typename T>
+__device__ void quantize_page_float(QuantSmemT<T> &sm, uint8_t *__restrict__ dst, float ks, float vs)
 {
 #pragma clang fp contract(off)
+    static_assert(!DEQUANT || sizeof(T) == 4, "dequantized values are written back as binary32");
     using FL = FloatLayout<FMT>;
+    using E = TileElem<T>;
+    constexpr int kTileStride = QuantSmemT<T>::kStride;
     const int tid = threadIdx.x;
     uint32_t *k32 = reinterpret_cast<uint32_t *>(dst);
     uint32_t *v32 = reinterpret_cast<uint32_t *>(dst + FL::kV);
@@ -232,10 +314,10 @@ __device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, fl
         // K: token-major
         {
             const int t = d / (kHeadDim / kPer), c0 = (d % (kHeadDim / kPer)) * kPer;
+            T *x = &sm.k[t * kTileStride + c0];
             uint32_t w = 0;
             if constexpr (FMT == kLayerFp8) {
-                float *x = &sm.k[t * kTileStride + c0];
-                w = e4m3_pair(x[0] / ks, x[1] / ks) | (e4m3_pair(x[2] / ks, x[3] / ks) << 16);
+                w = e4m3_pair(E::get(x) / ks, E::get(x + 1) / ks) | (e4m3_pair(E::get(x + 2) / ks, E::get(x + 3) / ks) << 16);
                 if constexpr (DEQUANT) {
 #pragma unroll
                     for (int i = 0; i < kPer; ++i) x[i] = e4m3_to_f32((w >> (8 * i)) & 0xFFu) * ks;
@@ -243,10 +325,9 @@ __device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, fl
             } else {
 #pragma unroll
                 for (int i = 0; i < kPer; ++i) {
-                    float &x = sm.k[t * kTileStride + c0 + i];
-                    const uint32_t b = float_to_bf16_bits(x);
+                    const uint32_t b = float_to_bf16_bits(E::get(x + i));
                     w |= b << (16 * i);
-                    if constexpr (DEQUANT) x = bf16_bits_to_float(static_cast<uint16_t>(b));
+                    if constexpr (DEQUANT) x[i] = bf16_bits_to_float(static_cast<uint16_t>(b));
                 }
             }
             k32[d] = w;
@@ -254,11 +335,11 @@ __device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, fl
         // V: channel-major
         {
             const int c = d / (kGroup / kPer), t0 = (d % (kGroup / kPer)) * kPer;
+            T *x0 = &sm.v[t0 * kTileStride + c];
             uint32_t w = 0;
             if constexpr (FMT == kLayerFp8) {
-                float *x0 = &sm.v[t0 * kTileStride + c];
-                w = e4m3_pair(x0[0] / vs, x0[kTileStride] / vs) |
-                    (e4m3_pair(x0[2 * kTileStride] / vs, x0[3 * kTileStride] / vs) << 16);
+                w = e4m3_pair(E::get(x0) / vs, E::get(x0 + kTileStride) / vs) |
+                    (e4m3_pair(E::get(x0 + 2 * kTileStride) / vs, E::get(x0 + 3 * kTileStride) / vs) << 16);
                 if constexpr (DEQUANT) {
 #pragma unroll
                     for (int i = 0; i < kPer; ++i) x0[i * kTileStride] = e4m3_to_f32((w >> (8 * i)) & 0xFFu) * vs;
@@ -266,10 +347,9 @@ __device__ void quantize_page_float(QuantSmem &sm, uint8_t *__restrict__ dst, fl
             } else {
 #pragma unroll
                 for (int i = 0; i < kPer; ++i) {
-                    float &x = sm.v[(t0 + i) * kTileStride + c];
-                    const uint32_t b = float_to_bf16_bits(x);
+                    const uint32_t b = float_to_bf16_bits(E::get(x0 + i * kTileStride));
                     w |= b << (16 * i);
-                    if constexpr (DEQUANT) x = bf16_bits_to_float(static_cast<uint16_t>(b));
+                    if constexpr (DEQUANT) x0[i * kTileStride] = bf16_bits_to_float(static_cast<uint16_t>(b));
                 }
             }
             v32[d] = w;

@@ -9,8 +9,8 @@
 //    section 4; reply to reviewer 2, section 2; reply to reviewer 3, section 1]
 //
 // One workgroup of 256 threads quantizes one page of one KV head: the 32 x 128 K and V
-// tiles are staged in LDS as binary32 (coalesced 8/16-byte loads, 16 threads per 256-byte
-// token row), then the page codec of kvq_codec.h encodes and packs them.  Layers kept in
+// tiles are staged in LDS (coalesced 16-byte loads; a bfloat16 source is staged as it is, an
+// fp32 source as binary32), then the page codec of kvq_codec.h encodes and packs them.  Layers kept in
 // FP8 (E4M3 of x / scale, one K and one V scale per KV head) or BF16 go through the
 // floating-point page codec instead.
 //   [When should you use mixed-precision KV caching to preserve accuracy in sensitive
@@ -24,55 +24,46 @@ namespace {
 
 constexpr int kThreads = kCodecThreads;
 
+// bf16 residual value of a source element (round to nearest even from fp32)
 template <typename SrcT>
 struct Src;
 
 template <>
 struct Src<uint16_t> {   // bf16 bit patterns
-    static constexpr int kVec = 8;   // elements per 16-byte load
-    __device__ static void load(const uint16_t *p, float *out)
-    {
-        const uint4 u = *reinterpret_cast<const uint4 *>(p);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = __uint_as_float(w[i] << 16);
-            out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-    }
     __device__ static uint16_t to_bf16(uint16_t x) { return x; }
 };
 
 template <>
 struct Src<float> {
-    static constexpr int kVec = 4;
-    __device__ static void load(const float *p, float *out)
-    {
-        const float4 f = *reinterpret_cast<const float4 *>(p);
-        out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
-    }
     __device__ static uint16_t to_bf16(float x) { return float_to_bf16_bits(x); }
 };
 
-// Stage rows [0, ntok) of a 32-token tile whose token rows are `row_stride` elements apart.
+// Stage a 32-token tile whose token rows are `row_stride` elements apart, in the source's
+// own element type (16-byte chunks, 16 or 32 threads per token row).
 template <typename SrcT>
-__device__ void stage_tile(const SrcT *__restrict__ src, long long row_stride, float *tile)
+__device__ void stage_tile(const SrcT *__restrict__ src, long long row_stride, SrcT *tile)
 {
-    constexpr int V = Src<SrcT>::kVec;
+    constexpr int V = 16 / sizeof(SrcT);
     constexpr int kChunks = kGroup * kHeadDim / V;
+    constexpr int kStride = QuantSmemT<SrcT>::kStride;
     for (int i = threadIdx.x; i < kChunks; i += kThreads) {
         const int t = i / (kHeadDim / V);
         const int c = (i % (kHeadDim / V)) * V;
-        float x[V];
-        Src<SrcT>::load(src + t * row_stride + c, x);
-#pragma unroll
-        for (int e = 0; e < V; ++e) tile[t * kTileStride + c + e] = x[e];
+        const uint4 x = *reinterpret_cast<const uint4 *>(src + t * row_stride + c);
+        if constexpr (sizeof(SrcT) == 2) {
+            *reinterpret_cast<uint4 *>(&tile[t * kStride + c]) = x;
+        } else {   // padded binary32 rows are not 16-byte aligned
+            tile[t * kStride + c] = __uint_as_float(x.x);
+            tile[t * kStride + c + 1] = __uint_as_float(x.y);
+            tile[t * kStride + c + 2] = __uint_as_float(x.z);
+            tile[t * kStride + c + 3] = __uint_as_float(x.w);
+        }
     }
 }
 
 // One page-head from the staged tiles, in the layer's format (KM: layer code).
-template <int KB, int VB, int KM>
-__device__ __forceinline__ void encode_page(QuantSmem &sm, uint8_t *pages, const float *scales, int phys, int H, int h)
+template <int KB, int VB, int KM, typename T>
+__device__ __forceinline__ void encode_page(QuantSmemT<T> &sm, uint8_t *pages, const float *scales, int phys, int H, int h)
 {
     uint8_t *dst = pages + (static_cast<long long>(phys) * H + h) * layer_page_bytes<KB, VB, KM>();
     if constexpr (is_float_layer(KM))
@@ -85,7 +76,7 @@ __device__ __forceinline__ void encode_page(QuantSmem &sm, uint8_t *pages, const
 template <int KB, int VB, int KM, typename SrcT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 {
-    __shared__ QuantSmem sm;
+    __shared__ QuantSmemT<SrcT> sm;
     const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int L = p.seq_len[b];
     if (L < 0 || L > p.max_tokens || L > kGroup * p.max_pages) return;
@@ -120,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 template <int KB, int VB, int KM>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p)
 {
-    __shared__ QuantSmem sm;
+    __shared__ QuantSmemT<uint16_t> sm;
     const int h = blockIdx.x, b = blockIdx.y;
     const int pos = p.pos[b];
     if (pos < 0 || pos >= kGroup * p.max_pages) return;
@@ -137,12 +128,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p)
     // the group is complete: quantize the 31 older residual tokens plus the new one
     const int phys = p.block_table[static_cast<long long>(b) * p.max_pages + pos / kGroup];
     if (phys < 0 || phys >= p.n_pages) return;
+    constexpr int kStride = QuantSmemT<uint16_t>::kStride;
     for (int i = tid; i < kGroup * kHeadDim; i += kThreads) {
         const int t = i / kHeadDim, c = i % kHeadDim;
-        const uint16_t kb16 = (t == kGroup - 1) ? p.k_new[nb + c] : p.resid_k[rbase + i];
-        const uint16_t vb16 = (t == kGroup - 1) ? p.v_new[nb + c] : p.resid_v[rbase + i];
-        sm.k[t * kTileStride + c] = bf16_bits_to_float(kb16);
-        sm.v[t * kTileStride + c] = bf16_bits_to_float(vb16);
+        sm.k[t * kStride + c] = (t == kGroup - 1) ? p.k_new[nb + c] : p.resid_k[rbase + i];
+        sm.v[t * kStride + c] = (t == kGroup - 1) ? p.v_new[nb + c] : p.resid_v[rbase + i];
     }
     __syncthreads();
     encode_page<KB, VB, KM>(sm, static_cast<uint8_t *>(p.pages), p.scales, phys, p.H, h);

@@ -83,7 +83,7 @@ struct QuantSmemT<uint16_t> {
 using QuantSmem = QuantSmemT<float>;
 constexpr int kTileStride = QuantSmem::kStride;
 
-// The 32 values of one group, `stride` elements apart, as binary32 (-0 becomes +0).
+// The 32 values of one group, `stride` elements apart, as binary32.
 template <typename T>
 __device__ __forceinline__ void load_group(const T *x, int stride, float (&v)[kGroup])
 {
@@ -95,15 +95,15 @@ __device__ __forceinline__ void load_group(const T *x, int stride, float (&v)[kG
                 const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[8 * q + 2 * e] = __uint_as_float(w[e] << 16) + 0.0f;
-                    v[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u) + 0.0f;
+                    v[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
+                    v[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
                 }
             }
             return;
         }
     }
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) v[i] = TileElem<T>::get(x + i * stride) + 0.0f;
+    for (int i = 0; i < kGroup; ++i) v[i] = TileElem<T>::get(x + i * stride);
 }
 
 // Codec of one 32-value group held by one thread (its values v, read by load_group).
@@ -116,30 +116,56 @@ __device__ __forceinline__ void encode_group(const float (&v)[kGroup], T *x, int
 {
 #pragma clang fp contract(off)
     static_assert(!DEQUANT || sizeof(T) == 4, "dequantized values are written back as binary32");
-    // the values are finite and -0 is gone, so the hardware min / max (v_min3 / v_max3
-    // after contraction) give exactly the comparison-based extremes
+    // the values are finite, so the hardware min / max (v_min3 / v_max3 after contraction)
+    // give the comparison-based extremes up to the sign of a zero; + 0 makes -0 into +0
+    // (and that is all a -0 value changes: v - z and the codes are the same for +-0)
     float mn = v[0], mx = v[0];
 #pragma unroll
     for (int i = 1; i < kGroup; ++i) {
         mn = __builtin_fminf(mn, v[i]);
         mx = __builtin_fmaxf(mx, v[i]);
     }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
     constexpr float levels = static_cast<float>((1 << BITS) - 1);
     const float s32 = (mx - mn) / levels;
     const uint16_t s16 = float_to_half_bits(s32);
     const uint16_t z16 = float_to_half_bits(mn);
     const float s = half_bits_to_float(s16);
     const float z = half_bits_to_float(z16);
+    // The code is rne(q), q = (v - z) / s correctly rounded, clamped to [0, levels]; a zero
+    // scale gives code 0.  For the finite scales of an fp16 word q comes from the
+    // reciprocal: y = RN(1/s) is the hardware reciprocal (within 1 ulp) after one Newton
+    // step (this holds for every significand that is not all ones, so for every fp16
+    // value -- checked exhaustively), q0 = RN(d y), and two corrections
+    // q <- q + (d - s q) y with exact residuals make it RN(d / s) (Markstein's theorem for
+    // the second; the first only has to make q faithful): five operations instead of the
+    // eleven of the general division, which remains for non-finite s or z (outside the
+    // input domain).  With s = 0, y = 0 makes every q 0.
+    float q[kGroup];
+    if (__builtin_isfinite(s) && __builtin_isfinite(z)) {
+        const float y0 = __builtin_amdgcn_rcpf(s);
+        const float y = s != 0.0f ? __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            const float d = v[i] - z;
+            const float q0 = d * y;
+            const float q1 = __builtin_fmaf(__builtin_fmaf(-s, q0, d), y, q0);
+            q[i] = __builtin_fmaf(__builtin_fmaf(-s, q1, d), y, q1);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) q[i] = s != 0.0f ? (v[i] - z) / s : 0.0f;
+    }
+    // rne and clamp in one add and one v_med3_f32: q + 2^23 rounds to the nearest integer
+    // (ties to even) for 0 <= q < 2^23, anything below 2^23 clamps to code 0, and the code
+    // is then the low bits of the result
+    constexpr float kMagic = 8388608.0f;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
-        uint32_t code = 0;
-        if (s != 0.0f) {
-            const float q = (v[i] - z) / s;
-            // round half to even, then clamp to [0, levels] (one v_med3_f32)
-            code = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(__builtin_rintf(q), 0.0f, levels));
-        }
-        codes[i * code_stride] = static_cast<uint8_t>(code);
-        if constexpr (DEQUANT) x[i * stride] = __builtin_fmaf(static_cast<float>(code), s, z);
+        const float f = __builtin_amdgcn_fmed3f(q[i] + kMagic, kMagic, kMagic + levels);
+        codes[i * code_stride] = static_cast<uint8_t>(__float_as_uint(f));
+        if constexpr (DEQUANT) x[i * stride] = __builtin_fmaf(f - kMagic, s, z);
     }
     sz_word = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
 }

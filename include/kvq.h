@@ -72,7 +72,8 @@
  *
  * Conventions.
  *   - Every device pointer is owned by the caller.  The library never allocates device
- *     memory, keeps no pointer after returning and has no mutable global state.
+ *     memory, keeps no pointer after returning and has no mutable global state (apart from
+ *     the KVQ_DEBUG counter below).
  *   - Every entry point is asynchronous on `stream` (a hipStream_t; NULL is the default
  *     stream).  Arguments are validated on the host before anything is launched; a
  *     nonzero status means nothing was launched.
@@ -82,6 +83,16 @@
  *     kernels never read or write outside the buffers the caller described.
  *   - Input values must be finite with |x| <= 65504 (fp16 range) so that scales and zeros
  *     are finite.
+ *   - KVQ_DEBUG: with this environment variable set to anything but "" or "0", every entry
+ *     point also checks, before its launch, what only the device holds: each length or
+ *     position against max_tokens / max_seq_len and the block table's capacity, the
+ *     block-table ids of the pages the call reads or writes against the pool, K / V values
+ *     of the live tokens and of the new token (finite, |x| <= 65504), q (finite) and the
+ *     FP8 scales (positive, finite).  A failed check returns KVQ_ERR_INVALID_ARG and
+ *     launches nothing.  The checks copy lengths and block table to the host and count
+ *     out-of-domain values in one device counter per GPU, so a checked call waits for its
+ *     stream, must not be captured into a graph, and checked calls on several streams of
+ *     one GPU at once share that counter.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -99,7 +110,8 @@ extern "C" {
 
 typedef enum kvq_status {
     KVQ_OK = 0,
-    KVQ_ERR_INVALID_ARG = 1,  /* null pointer, layer out of range, non-positive sizes    */
+    KVQ_ERR_INVALID_ARG = 1,  /* null pointer, layer out of range, non-positive sizes,
+                                 a failed KVQ_DEBUG check                               */
     KVQ_ERR_UNSUPPORTED = 2,  /* bits not in {2,4,8}, head_dim != 128, Hq % H != 0, ...   */
     KVQ_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned                  */
     KVQ_ERR_WORKSPACE = 4,    /* decode workspace missing or smaller than required        */

@@ -4,6 +4,7 @@
 
 #include "../../include/kvq.h"
 #include "kvq_codec.h"
+#include "kvq_debug.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -164,6 +165,10 @@ kvq_status kvq_pack(const kvq_model *model, int32_t layer, const kvq_layer_cache
     p.batch = cache->batch;
     p.max_tokens = max_tokens;
     p.max_pages = cache->max_pages;
+    if (kvq::debug_checks_enabled()) {
+        s = kvq::debug_check_pack(p, src_dtype == KVQ_F32, static_cast<hipStream_t>(stream));
+        if (s != KVQ_OK) return s;
+    }
     return hip_status(kvq::launch_pack(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                        src_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
 }
@@ -188,6 +193,10 @@ kvq_status kvq_append(const kvq_model *model, int32_t layer, const kvq_layer_cac
     p.H = model->n_kv_heads;
     p.batch = cache->batch;
     p.max_pages = cache->max_pages;
+    if (kvq::debug_checks_enabled()) {
+        s = kvq::debug_check_append(p, static_cast<hipStream_t>(stream));
+        if (s != KVQ_OK) return s;
+    }
     return hip_status(kvq::launch_append(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -253,6 +262,10 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     p.max_seq_len = max_seq_len;
     p.pages_per_split = pps;
     p.n_splits = n_splits;
+    if (kvq::debug_checks_enabled()) {
+        s = kvq::debug_check_decode(p, q_dtype == KVQ_F32, static_cast<hipStream_t>(stream));
+        if (s != KVQ_OK) return s;
+    }
     return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                          q_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
 }

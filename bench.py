@@ -293,6 +293,66 @@ def per_launch_durations(launch, n_items, reps):
     return [sum(evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)) / reps for i in range(n_items)]
 
 
+def quality_report(stack, n_seq=4):
+    """Quantization error of each distinct layer format, on the GPU, for the first n_seq
+    sequences (reported, not a pass/fail criterion): relative RMS error of the decoded K and
+    V (kvq_dequant) against the bf16 / fp32 source, and of the decode attention output
+    against plain fp32 attention over the unquantized tokens (the source plus the appended
+    token).  Runs after the timed region."""
+    import numpy as np
+    import torch
+    import synth
+    kvq = stack.kvq
+    cfg = stack.cfg
+    nb = min(n_seq, stack.B)
+    H, Hq, G = stack.H, stack.Hq, stack.Hq // stack.H
+    T = int(stack.lens[:nb].max())
+    L = T + 1
+    lens_d = torch.from_numpy(stack.attend[:nb].astype(np.int32)).to(stack.seq_len.device)
+    seen, rep = set(), {}
+    for l, spec in enumerate(stack.specs):
+        name = {2: "FP8", 3: "BF16"}.get(spec[2], f"K{spec[0]}V{spec[1]}" + ("-tok" if spec[2] == 1 else ""))
+        if name in seen:
+            continue
+        seen.add(name)
+        dev = stack.seq_len.device
+        cm = synth.outlier_mult(cfg["seed"], l, H, cfg["n_outliers"])
+        src = {}
+        for kind, key in ((synth.KIND_K, "k"), (synth.KIND_V, "v")):
+            x = synth.fill(cfg["seed"], kind, l, nb, T, H, chan_mult=cm if key == "k" else None,
+                           dtype=stack.src_dtype, device=dev).float()
+            new = (stack.k_new if key == "k" else stack.v_new)[l][:nb].float().view(nb, 1, H, 128)
+            full = torch.cat([x, new], dim=1)                     # [nb][L][H][128]
+            for b in range(nb):                                   # the new token sits at position lens[b]
+                lb = int(stack.lens[b])
+                full[b, lb] = new[b, 0]
+                full[b, lb + 1:] = 0.0
+            src[key] = full
+        cache = stack.caches[l].sub_batch(0, nb)
+        kd, vd = kvq.kvq_dequant(stack.model, l, cache, lens_d, L)
+        mask = (torch.arange(L, device=dev).view(1, L) < lens_d.view(nb, 1)).view(nb, L, 1, 1).float()
+        rel = {}
+        for key, d in (("k", kd), ("v", vd)):
+            err = (d - src[key]) * mask
+            rel[key] = float(err.square().sum().sqrt() / (src[key] * mask).square().sum().sqrt())
+        # fp32 attention over the unquantized tokens, every sequence at its own length
+        q = stack.q[l][:nb].float().view(nb, H, G, 128)
+        worst, num, den = 0.0, 0.0, 0.0
+        for b in range(nb):
+            lb = int(stack.attend[b])
+            kk = src["k"][b, :lb].permute(1, 2, 0).contiguous()      # [H][128][lb]
+            vv = src["v"][b, :lb].permute(1, 0, 2).contiguous()      # [H][lb][128]
+            s_ = torch.matmul(q[b], kk) * (1.0 / math.sqrt(128.0))   # [H][G][lb]
+            ref = torch.matmul(torch.softmax(s_, dim=-1), vv).view(Hq, 128)
+            got = stack.out[l][b]
+            worst = max(worst, float((got - ref).abs().max()))
+            num += float((got - ref).square().sum())
+            den += float(ref.square().sum())
+        rep[name] = {"layer": l, "k_rel_rms": rel["k"], "v_rel_rms": rel["v"],
+                     "attn_max_abs_vs_fp32": worst, "attn_rel_rms_vs_fp32": math.sqrt(num / den)}
+    return {"sequences": nb, "reference": "fp32 attention over the unquantized source tokens", "layers": rep}
+
+
 def cpu_baseline_decode(cfg, stack, n_seq):
     """The CPU oracle, as it stands (single thread), on the batch's first `n_seq` sequences
     for every layer: the same append + attention work of one decode step.  Packing the
@@ -409,6 +469,11 @@ def main():
 
     step_bytes = stack.alg_bytes(with_append)
     tokens_per_s = stack.B * 1000.0 / ms
+    quality = quality_report(stack) if with_append else None
+    if quality:
+        for name, r in quality["layers"].items():
+            log(f"[bench] {name} (layer {r['layer']}): K rel RMS {r['k_rel_rms']:.4f}, V {r['v_rel_rms']:.4f}; "
+                f"attention vs fp32 max abs {r['attn_max_abs_vs_fp32']:.2e}, rel RMS {r['attn_rel_rms_vs_fp32']:.4f}")
     cpu = None
     if args.cpu_seqs > 0 and args.config != "single":
         log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequences x {n_layers} layers ...")
@@ -450,6 +515,7 @@ def main():
                      "avg_launch_us_eager_events": sum(durs) / n_layers * 1e3,
                      "alg_bytes_per_launch": sum(dbytes) / n_layers},
         "cpu_baseline": cpu,
+        "quantization_error": quality,
     }
     print(json.dumps(rec), flush=True)
 

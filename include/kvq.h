@@ -201,6 +201,20 @@ kvq_status kvq_pack(const kvq_model *model, int32_t layer, const kvq_layer_cache
                     kvq_dtype src_dtype, const void *k_src, const void *v_src,
                     int32_t max_tokens, const int32_t *seq_len, void *stream);
 
+/* The inverse of the pack: one layer's cache back to binary32 K and V.
+ *   k_out, v_out: device fp32 [batch][max_tokens][n_kv_heads][128], 16-byte aligned
+ *   seq_len:      device int32 [batch]; tokens 0 .. seq_len[b] - 1 are written, the rest
+ *                 of k_out / v_out is left as it was
+ * Each value is what decode attention attends: code * s + z rounded once to binary32 for
+ * integer pages, E4M3 value * scale for FP8 pages, the bf16 value for BF16 pages and for
+ * the residual tokens.  A sequence whose length or page ids are invalid is skipped.
+ * For inspecting a cache, handing it to code that wants plain tensors, or measuring each
+ * layer's quantization error against its source.  [Mixed-precision KV-cache quantization
+ * per-layer sensitivity (llms-explorer.com), Facts] */
+kvq_status kvq_dequant(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                       int32_t max_tokens, const int32_t *seq_len, float *k_out, float *v_out,
+                       void *stream);
+
 /* Decode-time quantize-on-write of one new token per sequence for one layer.
  *   k_new, v_new: device bf16 [batch][n_kv_heads][128]
  *   pos:          device int32 [batch], the sequence length BEFORE this token

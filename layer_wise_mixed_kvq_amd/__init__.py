@@ -23,7 +23,7 @@ from ._native import (KVQ_BF16, KVQ_F32, KVQ_LAYER_BF16, KVQ_LAYER_FP8, KVQ_LAYE
 HEAD_DIM = 128
 GROUP = 32
 
-__all__ = ["Model", "KEYS_PER_CHANNEL", "KEYS_PER_TOKEN", "LAYER_INT", "LAYER_FP8", "LAYER_BF16", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
+__all__ = ["Model", "KEYS_PER_CHANNEL", "KEYS_PER_TOKEN", "LAYER_INT", "LAYER_FP8", "LAYER_BF16", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_dequant", "kvq_decode_attn", "kvq_append_decode_attn",
            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_head_page_bytes",
            "kvq_page_bytes", "kvq_equiv_bits", "kvq_format_version", "lib"]
 
@@ -174,6 +174,29 @@ def kvq_pack(model: Model, layer: int, cache: LayerCache, k_src, v_src, seq_len,
     check(lib().kvq_pack(ctypes.byref(model.c), layer, ctypes.byref(cs), _dtype_code(k_src),
                          k_src.data_ptr(), v_src.data_ptr(), k_src.shape[1], seq_len.data_ptr(),
                          _stream(stream)), "kvq_pack")
+
+
+def kvq_dequant(model: Model, layer: int, cache: LayerCache, seq_len, max_tokens: int, k_out=None, v_out=None,
+                stream=None):
+    """One layer's cache back to fp32 K, V [batch][max_tokens][n_kv_heads][128] (tokens past
+    seq_len[b] keep what k_out / v_out held; new tensors start at zero).  Returns (k, v)."""
+    import torch
+    _dev(seq_len, "seq_len")
+    if seq_len.dtype != torch.int32 or seq_len.numel() != cache.batch:
+        raise ValueError("seq_len must be int32 [batch]")
+    shape = (cache.batch, int(max_tokens), model.n_kv_heads, HEAD_DIM)
+    outs = []
+    for t, n in ((k_out, "k_out"), (v_out, "v_out")):
+        if t is None:
+            t = torch.zeros(shape, dtype=torch.float32, device=seq_len.device)
+        _dev(t, n)
+        if tuple(t.shape) != shape or t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32 {shape}")
+        outs.append(t)
+    cs = cache.c_struct()
+    check(lib().kvq_dequant(ctypes.byref(model.c), layer, ctypes.byref(cs), int(max_tokens), seq_len.data_ptr(),
+                            outs[0].data_ptr(), outs[1].data_ptr(), _stream(stream)), "kvq_dequant")
+    return outs[0], outs[1]
 
 
 def kvq_append(model: Model, layer: int, cache: LayerCache, k_new, v_new, pos, stream=None) -> None:

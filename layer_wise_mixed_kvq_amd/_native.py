@@ -14,7 +14,7 @@ KVQ_BF16, KVQ_F32 = 0, 1
 KVQ_LAYER_INT, KVQ_LAYER_FP8, KVQ_LAYER_BF16 = 0, 1, 2
 
 EXPORTED = ("kvq_status_str", "kvq_format_version", "kvq_head_page_bytes", "kvq_page_bytes",
-            "kvq_equiv_bits", "kvq_validate_model", "kvq_pack", "kvq_append",
+            "kvq_equiv_bits", "kvq_validate_model", "kvq_pack", "kvq_append", "kvq_dequant",
             "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_decode_attn", "kvq_append_decode_attn")
 
 
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_pack.restype = ctypes.c_int
         L.kvq_append.argtypes = [mp, i32, cp, vp, vp, vp, vp]
         L.kvq_append.restype = ctypes.c_int
+        L.kvq_dequant.argtypes = [mp, i32, cp, i32, vp, vp, vp, vp]
+        L.kvq_dequant.restype = ctypes.c_int
         L.kvq_decode_workspace_bytes.argtypes = [mp, i32, i32, i32]
         L.kvq_decode_workspace_bytes.restype = sz
         L.kvq_workspace_init.argtypes = [vp, sz, vp]

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
 # (source, extra flags): the decode kernels build in one translation unit per key bit width
-UNITS = [("kvq_api.hip", []), ("kvq_debug.hip", []), ("kvq_quant.hip", []), ("kvq_decode.hip", ["-DKVQ_DECODE_COMMON"]),
+UNITS = [("kvq_api.hip", []), ("kvq_debug.hip", []), ("kvq_quant.hip", []), ("kvq_dequant.hip", []), ("kvq_decode.hip", ["-DKVQ_DECODE_COMMON"]),
          ("kvq_decode.hip", ["-DKVQ_DECODE_KB=2"]), ("kvq_decode.hip", ["-DKVQ_DECODE_KB=4"]),
          ("kvq_decode.hip", ["-DKVQ_DECODE_KB=8"]), ("kvq_decode.hip", ["-DKVQ_DECODE_KB=16"])]
 

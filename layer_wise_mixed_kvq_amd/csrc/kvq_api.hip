@@ -5,6 +5,7 @@
 #include "../../include/kvq.h"
 #include "kvq_codec.h"
 #include "kvq_debug.h"
+#include "kvq_dequant.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -199,6 +200,36 @@ kvq_status kvq_append(const kvq_model *model, int32_t layer, const kvq_layer_cac
     }
     return hip_status(kvq::launch_append(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                          static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_dequant(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache, int32_t max_tokens,
+                       const int32_t *seq_len, float *k_out, float *v_out, void *stream)
+{
+    kvq_status s = check_layer(model, layer, cache);
+    if (s != KVQ_OK) return s;
+    if (!seq_len || !k_out || !v_out || max_tokens < 0) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_out) || !aligned16(v_out)) return KVQ_ERR_ALIGNMENT;
+    if (max_tokens == 0) return KVQ_OK;
+    kvq::DequantParams p;
+    p.seq_len = seq_len;
+    p.block_table = cache->block_table;
+    p.pages = cache->pages;
+    p.resid_k = cache->resid_k;
+    p.resid_v = cache->resid_v;
+    p.scales = scales_of(model, layer, cache);
+    p.k_out = k_out;
+    p.v_out = v_out;
+    p.n_pages = cache->n_pages;
+    p.H = model->n_kv_heads;
+    p.batch = cache->batch;
+    p.max_tokens = max_tokens;
+    p.max_pages = cache->max_pages;
+    if (kvq::debug_checks_enabled()) {
+        s = kvq::debug_check_dequant(p, static_cast<hipStream_t>(stream));
+        if (s != KVQ_OK) return s;
+    }
+    return hip_status(kvq::launch_dequant(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_model *model, int32_t batch, int32_t max_seq_len,

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "../../include/kvq.h"
+#include "kvq_dequant.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -16,5 +17,6 @@ bool debug_checks_enabled();
 kvq_status debug_check_pack(const PackParams &p, bool src_f32, hipStream_t s);
 kvq_status debug_check_append(const AppendParams &p, hipStream_t s);
 kvq_status debug_check_decode(const DecodeParams &p, bool q_f32, hipStream_t s);
+kvq_status debug_check_dequant(const DequantParams &p, hipStream_t s);
 
 }  // namespace kvq

@@ -185,4 +185,17 @@ kvq_status debug_check_decode(const DecodeParams &p, bool q_f32, hipStream_t s)
     return from_count(c.finish());
 }
 
+kvq_status debug_check_dequant(const DequantParams &p, hipStream_t s)
+{
+    std::vector<int32_t> len, bt;
+    if (!fetch(len, p.seq_len, static_cast<size_t>(p.batch), s)) return KVQ_ERR_HIP;
+    if (!fetch(bt, p.block_table, static_cast<size_t>(p.batch) * p.max_pages, s)) return KVQ_ERR_HIP;
+    for (int b = 0; b < p.batch; ++b) {
+        const int L = len[b];
+        if (L < 0 || L > p.max_tokens || L > kGroupTokens * p.max_pages) return KVQ_ERR_INVALID_ARG;
+        if (!ids_ok(bt, b, L / kGroupTokens, p.max_pages, p.n_pages)) return KVQ_ERR_INVALID_ARG;
+    }
+    return scales_ok(p.scales, p.H, s);
+}
+
 }  // namespace kvq

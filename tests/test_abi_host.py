@@ -135,6 +135,13 @@ def test_entry_points_reject_before_launch(kvq):
     assert L.kvq_append(mp, 0, ctypes.byref(good), None, A, A, None) == N.KVQ_ERR_INVALID_ARG
     assert L.kvq_append(mp, 0, ctypes.byref(good), A + 4, A, A, None) == N.KVQ_ERR_ALIGNMENT
     assert L.kvq_append(mp, 9, ctypes.byref(good), A, A, A, None) == N.KVQ_ERR_INVALID_ARG
+    # dequant
+    assert L.kvq_dequant(mp, 0, ctypes.byref(good), 64, None, A, A, None) == N.KVQ_ERR_INVALID_ARG
+    assert L.kvq_dequant(mp, 0, ctypes.byref(good), 64, A, None, A, None) == N.KVQ_ERR_INVALID_ARG
+    assert L.kvq_dequant(mp, 0, ctypes.byref(good), -1, A, A, A, None) == N.KVQ_ERR_INVALID_ARG
+    assert L.kvq_dequant(mp, 0, ctypes.byref(good), 64, A, A + 4, A, None) == N.KVQ_ERR_ALIGNMENT
+    assert L.kvq_dequant(mp, 2, ctypes.byref(good), 64, A, A, A, None) == N.KVQ_ERR_INVALID_ARG
+    assert L.kvq_dequant(mp, 0, ctypes.byref(good), 0, A, A, A, None) == N.KVQ_OK
     # decode
     need = L.kvq_decode_workspace_bytes(mp, 2, 64, 0)
     assert need > 0

@@ -95,19 +95,21 @@ SWEEP_SHAPES = [(64, 128), (16, 512), (8, 1024), (16, 4096)]
 # while they are unchanged
 DECODE_SOURCES = ["layer_wise_mixed_kvq_amd/csrc/kvq_decode.hip", "layer_wise_mixed_kvq_amd/csrc/kvq_device.h",
                   "layer_wise_mixed_kvq_amd/csrc/kvq_internal.h", "layer_wise_mixed_kvq_amd/csrc/kvq_codec.h"]
+PACK_SOURCES = ["layer_wise_mixed_kvq_amd/csrc/kvq_quant.hip", "layer_wise_mixed_kvq_amd/csrc/kvq_device.h",
+                "layer_wise_mixed_kvq_amd/csrc/kvq_internal.h", "layer_wise_mixed_kvq_amd/csrc/kvq_codec.h"]
 COPY_BYTES = 1 << 30
 
 
-def measured_traffic(config):
-    """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE measurement of
-    this workload, or None when there is none or the kernel changed since it was taken."""
+def measured_traffic(config, kernel="decode_kernel", sources=DECODE_SOURCES):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE measurement
+    of this workload, or None when there is none or the kernel changed since it was taken."""
     from layer_wise_mixed_kvq_amd.profiling import source_hash
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{config}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != source_hash([os.path.join(ROOT, x) for x in DECODE_SOURCES]):
+    if rec.get("source_sha256_16") != source_hash([os.path.join(ROOT, x) for x in sources]):
         return None
     return rec["traffic_bytes_per_launch"]
 
@@ -276,6 +278,20 @@ def time_graph(g, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def replay_stats(g, reps):
+    """Median and minimum of `reps` single replays, each between its own event pair (after
+    the timed region; context for the mean over the timed steps)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return [t[len(t) // 2], t[0]]
+
+
 def per_launch_durations(launch, n_items, reps):
     """Event pairs around every launch, on the stream the kernels run on; a GPU-side sleep
     first lets the host queue every launch ahead of the GPU so only kernel time is seen."""
@@ -424,7 +440,9 @@ def main():
     log(f"[bench] building {args.config} cache ...")
     t0 = time.perf_counter()
     stack = DecodeStack(cfg, dev)
-    log(f"[bench] cache built in {time.perf_counter() - t0:.1f} s")
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    log(f"[bench] cache built in {build_s:.1f} s")
 
     with_append = args.config != "single"
     step_fn = (lambda: stack.step(with_append, fused=not args.unfused))
@@ -440,10 +458,12 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms, wall = e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
+        step_stats = None
     else:
         g = capture(step_fn)
         log("[bench] graph captured; timing")
         ms, wall = time_graph(g, args.steps, args.warmup)
+        step_stats = replay_stats(g, 20)
     # attention-only step, and the step with the append as its own launch (context)
     g_attn = capture(lambda: stack.step(False))
     ms_attn, _ = time_graph(g_attn, args.steps, 2)
@@ -508,6 +528,8 @@ def main():
         "attention_only_ms_per_step": ms_attn,
         "unfused_append_ms_per_step": ms_unfused,
         "wall_s_timed": wall,
+        "step_ms_median_min": step_stats,
+        "cache_build_s": build_s,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
                      "kernel": "decode_kernel (kvq_decode_attn)",
@@ -603,7 +625,8 @@ def bench_pack(cfg, args):
         "config": {"workload": cfg["workload"], "tokens": T, "layers": len(caches)},
         "total_gbps": (src_bytes + page_bytes) / (ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "pack_kernel (kvq_pack)",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("pack", "pack_kernel", PACK_SOURCES),
+                     "kernel": "pack_kernel (kvq_pack)",
                      "avg_launch_us": launch_us, "alg_bytes_per_launch": (src_bytes + page_bytes) / len(caches)},
         "cpu_baseline": None,
     }

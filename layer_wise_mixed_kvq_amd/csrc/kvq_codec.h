@@ -16,8 +16,9 @@
 //      per-token mode one (token, 32-channel group)), threads 128..255 each reduce one
 //      (token, 32-channel group) of the values -- every thread owns exactly one group, so
 //      the min/max needs no cross-thread reduction;
-//   2. each thread encodes its own 32 values (binary32 subtract and correctly rounded
-//      divide, round half to even, clamp) and writes the codes as bytes to LDS;
+//   2. each thread encodes its own 32 values (binary32 subtract, the correctly rounded
+//      quotient by the scale, round half to even, clamp) and writes the codes as bytes to
+//      LDS;
 //   3. all 256 threads pack the code bytes into the bit layout and store whole dwords.
 #ifndef KVQ_CODEC_H
 #define KVQ_CODEC_H

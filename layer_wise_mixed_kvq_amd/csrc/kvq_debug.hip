@@ -53,7 +53,7 @@ struct Counter {
     bool ok;
     explicit Counter(hipStream_t st) : s(st), ok(true)
     {
-        const unsigned long long zero = 0;
+        static const unsigned long long zero = 0;   // outlives the asynchronous copy
         ok = hip_ok(hipMemcpyToSymbolAsync(HIP_SYMBOL(g_out_of_domain), &zero, sizeof(zero), 0,
                                            hipMemcpyHostToDevice, s));
     }

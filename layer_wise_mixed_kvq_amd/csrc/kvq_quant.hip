@@ -102,7 +102,6 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
             const long long si = base + t * row_stride + c;
             p.resid_k[rbase + i] = Src<SrcT>::to_bf16(ks[si]);
             p.resid_v[rbase + i] = Src<SrcT>::to_bf16(vs[si]);
-            (void)c;
         }
     }
 }

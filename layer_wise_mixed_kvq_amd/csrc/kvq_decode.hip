@@ -336,15 +336,21 @@ struct WaveLds {
     // rows padded by 4 words so that the 128-bit A-operand reads of different head rows
     // fall into different LDS banks
     alignas(16) uint32_t qp[NP][4 * GS + 1][68];     // (q s) parts: [part][head, + zero row][pair]
-    alignas(16) uint32_t pp[NP][PG][4 * GS + 1][20]; // (p s) parts: [part][value group][head][pair]
-    float p[32][4 * GS];                             // softmax weights of the page: [token][head]
+    // (p s) parts, one block per value group: [part][head, + zero row][pair]; the block
+    // stride is 16 mod 64 words so that the four lane groups' writes (one value group each)
+    // fall into disjoint LDS banks
+    static constexpr int kPPBlock = NP * (4 * GS + 1) * 20;
+    static constexpr int kPPStride = kPPBlock + (80 - kPPBlock % 64) % 64;
+    alignas(16) uint32_t pp[PG][kPPStride];
+    float p[4 * GS][48];                             // softmax weights of the page: [head][token]
     float alpha[4 * GS];
     float bv[4][4 * GS];                             // value zero terms at the end: [group][head]
+    __device__ uint32_t *pp_row(int g, int part, int row) { return &pp[g][(part * (4 * GS + 1) + row) * 20]; }
 };
 
 template <int GS>
 struct MergeLds {
-    float o[kWaves][4 * GS][kHeadDim];
+    float o[kWaves][4 * GS][kHeadDim + 16];   // head rows 16 mod 64 words apart: the lane groups' writes miss each other's banks
     float m[kWaves][4 * GS];
     float l[kWaves][4 * GS];
 };
@@ -737,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
         for (int part = 0; part < NP; ++part) {     // zero rows: A operands of absent heads
             W.qp[part][HS][lane] = 0u;
-            if (lane < 16 * PG) W.pp[part][lane / 16][HS][lane % 16] = 0u;
+            if (lane < 16 * PG) W.pp_row(lane / 16, part, HS)[lane % 16] = 0u;
         }
         const int hr = 4 * (r16 & 3) + (r16 >> 2);             // head of A row r16
         // With few head slots the A-operand parts (hi / lo, or hi / mid / lo) share one
@@ -982,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 for (int blk = 0; blk < 2; ++blk) {
                     const float pv = __builtin_amdgcn_exp2f(s2[blk][i] - m_run[i]);
                     l_part[i] += pv;
-                    W.p[16 * blk + r16][4 * i + a] = pv;
+                    W.p[4 * i + a][16 * blk + r16] = pv;
                 }
             }
           if constexpr (FLT) {
@@ -992,19 +998,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 0; i < GS; ++i) {
                 const int hh = 4 * i + a;
-                const float p0 = W.p[2 * r16][hh], p1 = W.p[2 * r16 + 1][hh];
+                const float p0 = W.p[hh][2 * r16], p1 = W.p[hh][2 * r16 + 1];
                 if constexpr (KM == kLayerFp8) {
                     const uint32_t hi = split_hi(p0 * 16384.0f, p1 * 16384.0f);
-                    W.pp[0][0][hh][r16] = hi;
-                    W.pp[1][0][hh][r16] = split_lo(p0, 16384.0f, p1, 16384.0f, hi);
+                    W.pp_row(0, 0, hh)[r16] = hi;
+                    W.pp_row(0, 1, hh)[r16] = split_lo(p0, 16384.0f, p1, 16384.0f, hi);
                 } else {
-                    split3_bf16(p0, p1, W.pp[0][0][hh][r16], W.pp[1][0][hh][r16], W.pp[2][0][hh][r16]);
+                    split3_bf16(p0, p1, W.pp_row(0, 0, hh)[r16], W.pp_row(0, 1, hh)[r16], W.pp_row(0, 2, hh)[r16]);
                 }
             }
             wave_lds_sync();
             uint4 av[NP];
 #pragma unroll
-            for (int part = 0; part < (RS ? 1 : NP); ++part) av[part] = lds_read16(&W.pp[RS ? apart : part][0][arow][4 * a]);
+            for (int part = 0; part < (RS ? 1 : NP); ++part) av[part] = lds_read16(&W.pp_row(0, RS ? apart : part, arow)[4 * a]);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 if constexpr (KM == kLayerFp8) {
@@ -1043,10 +1049,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 const float zv1 = half_bits_to_float(cur.vszw[1] >> 16);
 #pragma unroll
                 for (int hh = 0; hh < HS; ++hh) {
-                    const float p0 = W.p[t0][hh], p1 = W.p[t1][hh];
+                    const float p0 = W.p[hh][t0], p1 = W.p[hh][t1];
                     const uint32_t hi = split_hi(p0 * sv0, p1 * sv1);
-                    W.pp[0][a][hh][r16] = hi;
-                    W.pp[1][a][hh][r16] = split_lo(p0, sv0, p1, sv1, hi);
+                    W.pp_row(a, 0, hh)[r16] = hi;
+                    W.pp_row(a, 1, hh)[r16] = split_lo(p0, sv0, p1, sv1, hi);
                     zb[hh] = fmaf(p0, zv0, fmaf(p1, zv1, zb[hh]));
                 }
             }
@@ -1054,8 +1060,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             // ---- values on MFMA ------------------------------------------------------
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint4 ahi = lds_read16(&W.pp[RS ? apart : 0][g][arow][4 * a]);
-                const uint4 alo = RS ? ahi : lds_read16(&W.pp[1][g][arow][4 * a]);
+                const uint4 ahi = lds_read16(&W.pp_row(g, RS ? apart : 0, arow)[4 * a]);
+                const uint4 alo = RS ? ahi : lds_read16(&W.pp_row(g, 1, arow)[4 * a]);
 #pragma unroll
                 for (int nb = 2 * g; nb < 2 * g + 2; ++nb) {
                     const uint4 bv = unpack_b<VB>(cur.vc, nb, magic);

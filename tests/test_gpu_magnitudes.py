@@ -13,8 +13,9 @@ cores.  These cases drive those exponents far from the N(0,1) workloads:
   * pages whose every key channel is constant over the page and values whose every
     32-channel group is constant: every scale is 0 and the zeros carry the values.
 
-Powers of two keep the bf16 inputs exact.  Both sides quantize the scaled inputs, so the
-cache is the same bytes on both sides.  Attention is linear in V: outputs of values scaled
+Powers of two keep the bf16 inputs exact.  Both sides quantize the scaled inputs and the
+packed pages must be the same bytes (the pack's quotient by a subnormal fp16 scale
+included).  Attention is linear in V: outputs of values scaled
 by c are compared at the bar scaled by c.  That is the same relative accuracy the fp32 path
 holds on unit-scale values, so a path that flushed a subnormal scale to zero or lost
 an exponent would fail it.  The lse does not depend on V and keeps its own bar.
@@ -22,7 +23,7 @@ an exponent would fail it.  The lse does not depend on V and keeps its own bar.
 import numpy as np
 import pytest
 
-from kvq_cases import ATOL, LSE_RTOL, Case, log
+from kvq_cases import ATOL, LSE_RTOL, Case, host_array, live_resid_equal, log
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +64,9 @@ def _run(kvq, orc, c, v_scale, what):
     c.oracle_pack(orc)
     c.device_setup(kvq)
     c.device_pack(kvq)
+    assert np.array_equal(c.cache.pages.cpu().numpy(), c.o_pages), f"{what}: packed pages differ"
+    assert live_resid_equal(host_array(c.cache.resid_k), c.o_rk, c.lens), f"{what}: K residual differs"
+    assert live_resid_equal(host_array(c.cache.resid_v), c.o_rv, c.lens), f"{what}: V residual differs"
     o_ref, l_ref = c.oracle_decode(orc)
     for pps in (0, 2):
         out, lse = c.device_decode(kvq, pages_per_split=pps)

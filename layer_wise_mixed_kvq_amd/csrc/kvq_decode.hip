@@ -43,6 +43,10 @@
 //   values:  D[head][channel] = A(p s hi|lo, from LDS)    x B(value codes, chunk layout)
 // With G <= 8 the hi and lo parts occupy different rows of one A operand (parts x head
 // slots <= 16), so one MFMA per B operand forms both and the parts are summed afterwards.
+// Integer layers: score column r of blocks 0 and 1 holds not tokens r and 16 + r but the
+// two tokens (t0, t1) whose products lane r of each lane group packs into one A-operand
+// word of the values, so a lane folds its own softmax weights into all four value groups'
+// A operands and only that write goes through LDS.
 //
 // Floating-point layers (FP8 E4M3 with one K and one V scale per KV head, or BF16) hold
 // the values themselves, so nothing is folded per page: the scales multiply the scores
@@ -182,14 +186,6 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v)
     v = max(v, dpp<kQuadXor2>(v));
     v = max(v, dpp<kRowHalfMirror>(v));
     return max(v, dpp<kRowMirror>(v));
-}
-
-// maximum over the whole wave of a value that is already uniform within each lane group
-__device__ __forceinline__ uint32_t groups_max_u32(uint32_t v)
-{
-    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return max(max(a, b), max(c, d));
 }
 
 template <typename QT>
@@ -336,14 +332,10 @@ struct WaveLds {
     // rows padded by 4 words so that the 128-bit A-operand reads of different head rows
     // fall into different LDS banks
     alignas(16) uint32_t qp[NP][4 * GS + 1][68];     // (q s) parts: [part][head, + zero row][pair]
-    // (p s) parts, one block per value group: [part][head, + zero row][pair]; the block
-    // stride is 16 mod 64 words so that the four lane groups' writes (one value group each)
-    // fall into disjoint LDS banks
+    // (p s) parts, one block per value group: [part][head, + zero row][pair]
     static constexpr int kPPBlock = NP * (4 * GS + 1) * 20;
-    static constexpr int kPPStride = kPPBlock + (80 - kPPBlock % 64) % 64;
-    alignas(16) uint32_t pp[PG][kPPStride];
-    float p[4 * GS][48];                             // softmax weights of the page: [head][token]
-    float alpha[4 * GS];
+    alignas(16) uint32_t pp[PG][kPPBlock];
+    float p[4 * GS][48];                             // FP8 / BF16 layers: the page's softmax weights, [head][token]
     float bv[4][4 * GS];                             // value zero terms at the end: [group][head]
     __device__ uint32_t *pp_row(int g, int part, int row) { return &pp[g][(part * (4 * GS + 1) + row) * 20]; }
 };
@@ -533,12 +525,13 @@ __device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS, KM> &sm, c
 // ------------------------------------------------------------------------------------
 template <int KB, int VB>
 struct PageRegs {
-    uint32_t kc[2][KB];      // key codes of tokens 16*blk + (lane % 16), k-group lane / 16
+    uint32_t kc[2][KB];      // key codes of token t0 (blk 0) / t1 (blk 1) of the lane's value
+                             // pair, k-group lane / 16
     uint32_t vc[2 * VB];     // value code chunk `lane`
     uint32_t kszw[2];        // key (s, z) of the two channels this lane folds into q
     uint32_t kszb[8];        // key (s, z) of channels 8*(lane%16) .. +7 (zero terms, page max);
-                             // per-token keys: (s, z) of groups 0..3 of tokens r16, 16 + r16
-    uint32_t vszw[2];        // value (s, z) of the two tokens this lane folds into p
+                             // per-token keys: (s, z) of groups 0..3 of tokens t0, t1
+    uint32_t vszq[2][4];     // value (s, z) of groups 0..3 of tokens t0, t1
 };
 
 // Floating-point layers: kc[blk] holds channels 32a .. 32a+31 of token 16*blk + r16 (one
@@ -586,7 +579,7 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
     const int a = lane >> 4, r16 = lane & 15;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(base + PL::kKCodes + (16 * blk + r16) * PL::kKRowBytes + a * 4 * KB);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(base + PL::kKCodes + (blk == 0 ? t0 : t1) * PL::kKRowBytes + a * 4 * KB);
         if constexpr (KB == 2) {
             const uint2 x = *reinterpret_cast<const uint2 *>(src);
             r.kc[blk][0] = x.x; r.kc[blk][1] = x.y;
@@ -609,13 +602,15 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
         r.kszw[0] = ksz[ch0];
         r.kszw[1] = ksz[ch1];
     }
-    const uint4 b0 = *reinterpret_cast<const uint4 *>(ksz + (KT ? kValueGroups * r16 : 8 * r16));
-    const uint4 b1 = *reinterpret_cast<const uint4 *>(ksz + (KT ? kValueGroups * (16 + r16) : 8 * r16 + 4));
+    const uint4 b0 = *reinterpret_cast<const uint4 *>(ksz + (KT ? kValueGroups * t0 : 8 * r16));
+    const uint4 b1 = *reinterpret_cast<const uint4 *>(ksz + (KT ? kValueGroups * t1 : 8 * r16 + 4));
     r.kszb[0] = b0.x; r.kszb[1] = b0.y; r.kszb[2] = b0.z; r.kszb[3] = b0.w;
     r.kszb[4] = b1.x; r.kszb[5] = b1.y; r.kszb[6] = b1.z; r.kszb[7] = b1.w;
     const uint32_t *vsz = reinterpret_cast<const uint32_t *>(base + PL::kVSz);
-    r.vszw[0] = vsz[kValueGroups * t0 + a];
-    r.vszw[1] = vsz[kValueGroups * t1 + a];
+    const uint4 w0 = *reinterpret_cast<const uint4 *>(vsz + kValueGroups * t0);
+    const uint4 w1 = *reinterpret_cast<const uint4 *>(vsz + kValueGroups * t1);
+    r.vszq[0][0] = w0.x; r.vszq[0][1] = w0.y; r.vszq[0][2] = w0.z; r.vszq[0][3] = w0.w;
+    r.vszq[1][0] = w1.x; r.vszq[1][1] = w1.y; r.vszq[1][2] = w1.z; r.vszq[1][3] = w1.w;
     }
 }
 
@@ -831,9 +826,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
             m_run[i] = -INFINITY;
             l_part[i] = 0.0f;
         }
-        float zb[HS];
+        float zb[GS][4];                                        // value zero terms: head 4i + a, group j
 #pragma unroll
-        for (int hh = 0; hh < HS; ++hh) zb[hh] = 0.0f;
+        for (int i = 0; i < GS; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zb[i][j] = 0.0f;
         // The value accumulators hold sum_t (p s 2^ev) v: ev keeps the folded
         // weights in the normal fp16 range (|p s 2^ev| < 2^15); it only decreases, rescaling
         // acc when it does.
@@ -974,21 +971,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
                         for (int part = 0; part < (RS ? NP : 1); ++part) acc[nb][part * GS + i] *= alpha[i];
                     }
-                    if (!FLT && r16 == 0) W.alpha[4 * i + a] = alpha[i];
-                }
-                if constexpr (!FLT) {
-                    wave_lds_sync();
+                    if constexpr (!FLT) {
 #pragma unroll
-                    for (int hh = 0; hh < HS; ++hh) zb[hh] *= W.alpha[hh];
+                        for (int j = 0; j < 4; ++j) zb[i][j] *= alpha[i];
+                    }
                 }
             }
+            // integer layers: blk 0 / 1 of this lane are tokens t0 / t1, the value pair it folds
+            float pw[2][GS];
 #pragma unroll
             for (int i = 0; i < GS; ++i) {
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
                     const float pv = __builtin_amdgcn_exp2f(s2[blk][i] - m_run[i]);
                     l_part[i] += pv;
-                    W.p[4 * i + a][16 * blk + r16] = pv;
+                    pw[blk][i] = pv;
+                    if constexpr (FLT) W.p[4 * i + a][16 * blk + r16] = pv;
                 }
             }
           if constexpr (FLT) {
@@ -1026,8 +1024,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
           } else {
             // ---- value-scale exponent of this page -----------------------------------
             {
-                uint32_t vmax = max(cur.vszw[0] & 0x7FFFu, cur.vszw[1] & 0x7FFFu);
-                vmax = groups_max_u32(row_max_u32(vmax));
+                // every row of lanes holds all 32 tokens and all four groups
+                uint32_t vmax = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vmax = max(vmax, max(cur.vszq[0][j] & 0x7FFFu, cur.vszq[1][j] & 0x7FFFu));
+                vmax = row_max_u32(vmax);
                 if (vmax != 0u) {
                     int e;
                     frexpf(half_bits_to_float(vmax), &e);
@@ -1040,20 +1041,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     }
                 }
             }
-            wave_lds_sync();
-            // ---- fold value scales into p: two tokens x every head slot, hi/lo ----------
-            {
-                const float sv0 = ldexpf(half_bits_to_float(cur.vszw[0] & 0xFFFFu), ev - vshift);
-                const float sv1 = ldexpf(half_bits_to_float(cur.vszw[1] & 0xFFFFu), ev - vshift);
-                const float zv0 = half_bits_to_float(cur.vszw[0] >> 16);
-                const float zv1 = half_bits_to_float(cur.vszw[1] >> 16);
+            // ---- fold value scales into p: the lane's own weights of tokens t0, t1 x every
+            // value group, hi/lo (no exchange: the scores put this lane's pair in its registers)
 #pragma unroll
-                for (int hh = 0; hh < HS; ++hh) {
-                    const float p0 = W.p[hh][t0], p1 = W.p[hh][t1];
+            for (int j = 0; j < 4; ++j) {
+                const float sv0 = ldexpf(half_bits_to_float(cur.vszq[0][j] & 0xFFFFu), ev - vshift);
+                const float sv1 = ldexpf(half_bits_to_float(cur.vszq[1][j] & 0xFFFFu), ev - vshift);
+                const float zv0 = half_bits_to_float(cur.vszq[0][j] >> 16);
+                const float zv1 = half_bits_to_float(cur.vszq[1][j] >> 16);
+#pragma unroll
+                for (int i = 0; i < GS; ++i) {
+                    const float p0 = pw[0][i], p1 = pw[1][i];
                     const uint32_t hi = split_hi(p0 * sv0, p1 * sv1);
-                    W.pp_row(a, 0, hh)[r16] = hi;
-                    W.pp_row(a, 1, hh)[r16] = split_lo(p0, sv0, p1, sv1, hi);
-                    zb[hh] = fmaf(p0, zv0, fmaf(p1, zv1, zb[hh]));
+                    W.pp_row(j, 0, 4 * i + a)[r16] = hi;
+                    W.pp_row(j, 1, 4 * i + a)[r16] = split_lo(p0, sv0, p1, sv1, hi);
+                    zb[i][j] = fmaf(p0, zv0, fmaf(p1, zv1, zb[i][j]));
                 }
             }
             wave_lds_sync();
@@ -1093,9 +1095,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         for (int i = 0; i < GS; ++i) lw[i] = row_sum(l_part[i]);
         if constexpr (!FLT) {
 #pragma unroll
-            for (int hh = 0; hh < HS; ++hh) {
-                const float v = row_sum(zb[hh]);    // lanes of group a cover all 32 tokens once
-                if (r16 == 0) W.bv[a][hh] = v;
+            for (int i = 0; i < GS; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v = row_sum(zb[i][j]);    // the 16 lanes' pairs cover all 32 tokens once
+                    if (r16 == 0) W.bv[j][4 * i + a] = v;
+                }
             }
             wave_lds_sync();
         }

@@ -73,6 +73,19 @@ def test_per_token_key_row_layout(orc, kb):
                 o0, o1 = where[c0], where[c0 + 1]
                 assert o0 // 32 == o1 // 32, f"channels {c0}, {c0 + 1} not in one 32-bit word"
                 assert o1 - o0 == 16, f"channels {c0}, {c0 + 1} not 16 bits apart"
+    # the slot order the format states (n = 16/kb, hh = (s/n)%2, k = (s/(2n))*n + s%n,
+    # channel 32*(k/4) + 8*a + 2*(k%4) + hh), written out by hand for the first 16 slots
+    # of chunk 0 and checked for every slot of every chunk
+    by_slot = {off // kb: c for c, off in where.items()}
+    first16 = {2: [0, 2, 4, 6, 32, 34, 36, 38, 1, 3, 5, 7, 33, 35, 37, 39],
+               4: [0, 2, 4, 6, 1, 3, 5, 7, 32, 34, 36, 38, 33, 35, 37, 39],
+               8: [0, 2, 1, 3, 4, 6, 5, 7, 32, 34, 33, 35, 36, 38, 37, 39]}[kb]
+    assert [by_slot[s] for s in range(16)] == first16, f"kb={kb}: slot order of chunk 0"
+    n = 16 // kb
+    for a in range(4):
+        for s in range(32):
+            hh, k = (s // n) % 2, (s // (2 * n)) * n + s % n
+            assert by_slot[32 * a + s] == 32 * (k // 4) + 8 * a + 2 * (k % 4) + hh, f"kb={kb} chunk {a} slot {s}"
 
 
 @pytest.mark.parametrize("kb,vb", PAIRS)

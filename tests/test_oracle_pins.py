@@ -324,6 +324,45 @@ def test_packed_bytes_hand_derived(orc):
     assert np.array_equal(vc8, want)
 
 
+def _value_code_bits(orc, vb, cells):
+    """Bit offset, inside the V code section, of the code of each (token, channel) cell,
+    found by packing a tile whose only nonzero value is that cell (its group then spans
+    [0, 1]: the cell gets code 2^vb - 1, every other code is 0)."""
+    k = np.zeros((32, 128), dtype=np.float32)
+    base = 512 * 2 + 512
+    out = {}
+    for t, c in cells:
+        v = np.zeros((32, 128), dtype=np.float32)
+        v[t, c] = 1.0
+        page = orc.pack_page(k, v, 2, vb)
+        bits = np.unpackbits(page[base:base + 512 * vb], bitorder="little")
+        on = np.nonzero(bits)[0]
+        assert len(on) == vb and on[-1] - on[0] == vb - 1 and on[0] % vb == 0, f"vb={vb} ({t}, {c}): {on}"
+        out[(t, c)] = int(on[0])
+    return out
+
+
+@pytest.mark.parametrize("vb", BITS)
+def test_value_code_layout_one_hot(orc, vb):
+    """Every (token, channel) code sits where the format says: chunk 16*(t/8) + c%16 of
+    8*vb bytes; inside it, with i = t%8, j = i%4, k = 4*(c/16) + j, n = 16/vb, at bit
+    32*(k/n) + 16*(i/4) + vb*(k%n).  A few offsets are worked out by hand first."""
+    hand = {2: {(0, 0): 0, (5, 17): 154, (12, 100): 2672},
+            4: {(31, 127): 16380, (0, 16): 32, (9, 1): 17 * 256 + 4},
+            8: {(7, 3): 1592, (0, 0): 0, (8, 0): 16 * 512}}[vb]
+    got = _value_code_bits(orc, vb, list(hand))
+    assert got == hand, f"vb={vb}: {got} != {hand}"
+    cells = [(t, c) for t in range(32) for c in range(128)]
+    got = _value_code_bits(orc, vb, cells)
+    n = 16 // vb
+    for (t, c), off in got.items():
+        i, j = t % 8, t % 4
+        k = 4 * (c // 16) + j
+        want = (16 * (t // 8) + c % 16) * 64 * vb + 32 * (k // n) + 16 * (i // 4) + vb * (k % n)
+        assert off == want, f"vb={vb} ({t}, {c}): bit {off}, format says {want}"
+    assert sorted(got.values()) == [vb * x for x in range(4096)]
+
+
 @pytest.mark.parametrize("kb,vb", PAIRS)
 def test_page_round_trip_on_grid(orc, kb, vb):
     rng = np.random.default_rng(kb * 10 + vb)
@@ -509,10 +548,11 @@ def test_block_table_indirection(orc):
     assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
 
 
+@pytest.mark.parametrize("L", [63, 64, 70])
 @pytest.mark.parametrize("kb,vb", [(4, 2), (2, 8)])
-def test_prefill_equals_prefix_plus_appends(orc, kb, vb):
-    rng = np.random.default_rng(kb + vb)
-    B, H, L, k0 = 2, 2, 70, 25
+def test_prefill_equals_prefix_plus_appends(orc, kb, vb, L):
+    rng = np.random.default_rng(kb + vb + L)
+    B, H, k0 = 2, 2, 25
     maxp = 3
     k = _bf16_bits(rng.standard_normal((B, L, H, 128)))
     v = _bf16_bits(rng.standard_normal((B, L, H, 128)))

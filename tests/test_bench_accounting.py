@@ -62,3 +62,17 @@ def test_prefill_pack_bytes():
     pages = sum(T // 32 * H * _page(kb, vb) for kb, vb in cfg["pairs"])
     assert (src, pages) == (4_294_967_296, 1_140_850_688)
     assert (src + pages) / 32 == pytest.approx(169_869_312)
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """bench.py measures one GPU; asked for more (flag or launcher) it exits with status 2
+    and says why, before touching torch or the GPU."""
+    import os
+    import subprocess
+    import sys
+    e = dict(os.environ, **env)
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), *argv],
+                       capture_output=True, text=True, env=e, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr and r.stdout == ""

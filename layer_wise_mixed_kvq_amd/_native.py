@@ -9,6 +9,16 @@ import os
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
+
+def use_phase_timer_build(path=None) -> None:
+    """Load the profiling variant libkvq_phases.so (same sources, decode phase timers; or the
+    build at `path`) instead of libkvq.so; only the phase profiler calls this, before anything
+    loads the library."""
+    global _LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    _LIB_PATH = path or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq_phases.so")
+
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGNMENT, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(6)
 KVQ_BF16, KVQ_F32 = 0, 1
 KVQ_LAYER_INT, KVQ_LAYER_FP8, KVQ_LAYER_BF16 = 0, 1, 2
@@ -76,6 +86,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn.restype = ctypes.c_int
         L.kvq_append_decode_attn.argtypes = [mp, i32, cp, vp, vp, vp, ctypes.c_int, vp, i32, i32, vp, vp, vp, sz, vp]
         L.kvq_append_decode_attn.restype = ctypes.c_int
+        if hasattr(L, "kvq_profile_set_phase_buffer"):
+            L.kvq_profile_set_phase_buffer.argtypes = [vp, sz]
+            L.kvq_profile_set_phase_buffer.restype = None
         _lib = L
     return _lib
 

@@ -13,6 +13,18 @@ namespace kvq {
 int decode_max_g();
 }
 
+#if defined(KVQ_PHASE_TIMERS)
+namespace kvq {
+unsigned long long *g_phase_buf = nullptr;
+size_t g_phase_bytes = 0;
+}
+extern "C" void kvq_profile_set_phase_buffer(void *buf, size_t bytes)
+{
+    kvq::g_phase_buf = static_cast<unsigned long long *>(buf);
+    kvq::g_phase_bytes = buf ? bytes : 0;
+}
+#endif
+
 namespace {
 
 bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
@@ -293,6 +305,13 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     p.max_seq_len = max_seq_len;
     p.pages_per_split = pps;
     p.n_splits = n_splits;
+    p.phase_ts = nullptr;
+#if defined(KVQ_PHASE_TIMERS)
+    {
+        const size_t need = static_cast<size_t>(H) * cache->batch * n_splits * 4 * kvq::kPhaseStamps * 8;
+        if (kvq::g_phase_buf && kvq::g_phase_bytes >= need) p.phase_ts = kvq::g_phase_buf;
+    }
+#endif
     if (kvq::debug_checks_enabled()) {
         s = kvq::debug_check_decode(p, q_dtype == KVQ_F32, static_cast<hipStream_t>(stream));
         if (s != KVQ_OK) return s;

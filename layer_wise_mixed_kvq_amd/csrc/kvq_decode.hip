@@ -201,6 +201,30 @@ __device__ __forceinline__ float load_q<float>(const void *q, long long i)
     return static_cast<const float *>(q)[i];
 }
 
+// eight consecutive q elements from element i (a multiple of 8): one 16-byte load for bf16,
+// two for binary32
+template <typename QT>
+__device__ __forceinline__ void load_q8(const void *q, long long i, float (&out)[8]);
+template <>
+__device__ __forceinline__ void load_q8<uint16_t>(const void *q, long long i, float (&out)[8])
+{
+    const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + i);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[2 * k] = __uint_as_float(u[k] << 16);
+        out[2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load_q8<float>(const void *q, long long i, float (&out)[8])
+{
+    const float4 x = *reinterpret_cast<const float4 *>(static_cast<const float *>(q) + i);
+    const float4 y = *reinterpret_cast<const float4 *>(static_cast<const float *>(q) + i + 4);
+    out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    out[4] = y.x; out[5] = y.y; out[6] = y.z; out[7] = y.w;
+}
+
 // 1024.0 in both fp16 halves, opaque to the optimizer so that the unpack below stays one
 // bit-field insert (v_bfi_b32) instead of a constant-folded and + or.  The empty asm emits
 // no instruction: the register is written by an ordinary compiler-generated move.
@@ -360,26 +384,42 @@ struct ResidualOut {              // (m, l, o) of the residual tokens, kept for 
     float l[4 * GS];
 };
 
-// (m, l) of a chunk of split partials, staged for the final merge
-constexpr int kMergeChunk = 64;
-struct CombineLds {
-    float m[kMergeChunk][16];
-    float l[kMergeChunk][16];
-};
-
 template <int GS, int KM>
 struct DecodeSmem {
-    float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128)
-    int eq[4 * GS];               // per head: |qs * 2^eq| in [1, 2)
+    float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128), for the residual tokens
     ResidualOut<GS> ro;
     union {
         WaveLds<GS, KM> w[kWaves];
         MergeLds<GS> merge;
         ResidualLds<GS> res;
-        CombineLds comb;
     } u;
     int last;
+    int early;
 };
+
+#if defined(KVQ_PHASE_TIMERS)
+// Profiling build only: lane 0 of each wave records the 100 MHz real-time counter at the
+// kernel's phase boundaries (record layout beside kPhaseStamps in kvq_internal.h).
+__device__ __forceinline__ void phase_stamp(const DecodeParams &p, int k)
+{
+    if (p.phase_ts && (threadIdx.x & 63) == 0) {
+        const long long wg = blockIdx.x + static_cast<long long>(gridDim.x) * (blockIdx.y + static_cast<long long>(gridDim.y) * blockIdx.z);
+        unsigned long long *r = p.phase_ts + (wg * kWaves + (threadIdx.x >> 6)) * kPhaseStamps;
+        r[k] = __builtin_amdgcn_s_memrealtime();
+        if (k == 0) {
+            // HW_REG_HW_ID (id 4) and HW_REG_XCC_ID (id 20), all 32 bits
+            const unsigned hw = static_cast<unsigned>(__builtin_amdgcn_s_getreg(4 | (31 << 11)));
+            const unsigned xcc = static_cast<unsigned>(__builtin_amdgcn_s_getreg(20 | (31 << 11)));
+            r[6] = (static_cast<unsigned long long>(xcc & 0xFu) << 32) | hw;
+            r[7] = static_cast<unsigned long long>(blockIdx.x) | (static_cast<unsigned long long>(blockIdx.y) << 20) |
+                   (static_cast<unsigned long long>(blockIdx.z) << 40);
+        }
+    }
+}
+#define KVQ_STAMP(k) phase_stamp(p, k)
+#else
+#define KVQ_STAMP(k) ((void)0)
+#endif
 
 __device__ __forceinline__ uint4 lds_read16(const uint32_t *p)
 {
@@ -446,6 +486,7 @@ __device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS, KM> &sm, c
 {
     ResidualLds<GS> &R = sm.u.res;
     const int tid = threadIdx.x;
+    KVQ_STAMP(12);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int i = tid + k * kThreads, row = i / (kHeadDim / 8), col = 8 * (i % (kHeadDim / 8));
@@ -517,6 +558,7 @@ __device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS, KM> &sm, c
         sm.ro.o[h][c] = o;
     }
     __syncthreads();
+    KVQ_STAMP(13);
     return ok;
 }
 
@@ -616,8 +658,9 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
 
 // KM: the layer code -- integer codes with per-channel or per-token keys (one key group per
 // token and 32 channels), or FP8 / BF16 values
+// two waves per SIMD (two workgroups per CU) whenever G <= 8: at most 256 registers per lane
 template <int KB, int VB, int GS, typename QT, int KM>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 2 ? 2 : 1))) void decode_kernel(DecodeParams p)
 {
     constexpr bool KT = KM == kLayerKeysPerToken;
     constexpr bool FLT = is_float_layer(KM);
@@ -629,62 +672,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x;
     const int G = p.G;
+    KVQ_STAMP(0);
     const long long bh = static_cast<long long>(b) * p.H + h;
     float *out_bh = p.out + bh * G * kHeadDim;
     float *lse_bh = p.lse ? p.lse + bh * G : nullptr;
     const bool append = p.pos != nullptr;      // fused append: attend over pos + 1 tokens
-    const int L = append ? p.pos[b] + 1 : p.seq_len[b];
-    // ---- requests that do not depend on the length, issued before it arrives: this wave's
-    // block-table ids (every page the split could hold), q, and the wave's first page (its
-    // id checked against the pool; unused if the sequence turns out shorter) -------------
+    // ---- the length, this wave's block-table ids (every page the split could hold) and q
+    // are requested together, before any of them is waited for.  The length is read as a
+    // lane-indexed vector load (lane i: sequence 64*(b/64) + i) and taken from lane b % 64: a
+    // uniform scalar load would be waited for (with the kernel arguments) before the other
+    // requests could go out -------------------------------------------------------------
     const int wave = tid >> 6, lane = tid & 63;
+    const int a = lane >> 4, r16 = lane & 15;
     const int P = p.pages_per_split;
     const int pg_begin = split * P + wave;
-    const int pg_lim = min(p.max_pages, (split + 1) * P);
-    int my_phys = 0;
-    if (pg_begin + kWaves * lane < pg_lim)
-        my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + pg_begin + kWaves * lane];
-    // (unconditional loads at a clamped index: nothing waits on them until q is staged)
-    constexpr int kQPer = (HS * kHeadDim + kThreads - 1) / kThreads;
-    float qv[kQPer];
-#pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-        const int i = tid + k * kThreads;
-        qv[k] = load_q<QT>(p.q, bh * G * kHeadDim + (i < G * kHeadDim ? i : 0));
-    }
-
-    const bool bad_len = (append ? L <= 0 : L < 0) || L > p.max_seq_len || L > kGroup * p.max_pages;
-    if (bad_len || L == 0) {
-        if (split == 0) {
-            const float o = bad_len ? NAN : 0.0f;
-            for (int i = tid; i < G * kHeadDim; i += kThreads) out_bh[i] = o;
-            if (lse_bh && tid < G) lse_bh[tid] = bad_len ? NAN : -INFINITY;
-        }
-        return;
-    }
-    // a fused append that completes a group quantizes that page itself (split 0) and attends
-    // over it from LDS: the pool supplies only the pages that existed before this call
-    const bool flush = append && L % kGroup == 0;
-    const int full = L / kGroup - (flush ? 1 : 0);      // pages read from the pool
-    const int nres = flush ? kGroup : L % kGroup;       // tokens attended from the residual tile
-    const int n_ps = (full + P - 1) / P;               // splits with pages
-    const int n_work = n_ps > 0 ? n_ps : 1;             // workgroups of this (sequence, KV head)
-    if (split >= n_work) return;
-    // the residual tokens belong to split 0: the first workgroups dispatched absorb the extra
-    // work while the last ones are still starting
-    const bool has_res = nres > 0 && split == 0;
-
-    const int pg_end = min(full, (split + 1) * P);
-    const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
-    // q arrives with the block-table ids: stage it before the page and residual requests so
-    // that nothing waits on those until the page loop
-#pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-        const int i = tid + k * kThreads;
-        if (i < G * kHeadDim) sm.qs[i / kHeadDim][i % kHeadDim] = qv[k] * kScoreScale;
-    }
+    const int pg_lim = min(p.max_pages, (split + 1) * P);    // >= 1
     // lane roles in the page loop
-    const int a = lane >> 4, r16 = lane & 15;
     const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
     // per-channel keys: any channel pair of the lane's 32-channel group; per-token keys: the
     // pair 32*kjj + 8*kq + 2*kj, + 1, so that matrix-core block kjj is exactly key group kjj
@@ -696,6 +699,69 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     : KT                ? 32 * kjj + 8 * kq + 2 * (kj & 1) + (kj >> 1)
                                         : 32 * kq + key_pair_channel<KB>(kjj, kj);
     const int ch1 = FLT || (KT && KB == 8) ? ch0 + 1 : KT ? ch0 + 4 : ch0 + key_pair_step<KB>();
+    // (unconditional loads at clamped indices, in one basic block, none waited for before the
+    // last is issued; the length first, so that waiting for it leaves the others in flight)
+    const int *len_src = append ? p.pos : p.seq_len;
+    const int len_lane = len_src[min((b & ~63) + lane, p.batch - 1)];
+    const int bt_i = pg_begin + kWaves * lane;
+    int my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + min(bt_i, pg_lim - 1)];
+    // q straight from memory in the layouts the lane uses: 8 channels 8*r16 .. +7 of heads
+    // 4i + a (the zero terms; their maxima give the per-head exponents) and channels ch0, ch1
+    // of every head (the folded key pair); per-token keys also take channels 32J + 2*r16, +1
+    const long long q0 = bh * G * kHeadDim;
+    float qbl[GS][8], qwl[HS][2], qtl[KT ? GS : 1][4][2];
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+        const long long qi = q0 + min(4 * i + a, G - 1) * kHeadDim + 8 * r16;
+        load_q8<QT>(p.q, qi, qbl[i]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < HS; ++hh) {
+        const long long qh = q0 + min(hh, G - 1) * kHeadDim;
+        qwl[hh][0] = load_q<QT>(p.q, qh + ch0);
+        qwl[hh][1] = load_q<QT>(p.q, qh + ch1);
+    }
+    if constexpr (KT) {
+#pragma unroll
+        for (int i = 0; i < GS; ++i)
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const long long qi = q0 + min(4 * i + a, G - 1) * kHeadDim + 32 * J + 2 * r16;
+                qtl[i][J][0] = load_q<QT>(p.q, qi);
+                qtl[i][J][1] = load_q<QT>(p.q, qi + 1);
+            }
+    }
+    if (bt_i >= pg_lim) my_phys = 0;
+    const int L = __builtin_amdgcn_readlane(len_lane, b & 63) + (append ? 1 : 0);
+    KVQ_STAMP(8);
+
+    const bool bad_len = (append ? L <= 0 : L < 0) || L > p.max_seq_len || L > kGroup * p.max_pages;
+    if (bad_len || L == 0) {
+        if (split == 0) {
+            const float o = bad_len ? NAN : 0.0f;
+            for (int i = tid; i < G * kHeadDim; i += kThreads) out_bh[i] = o;
+            if (lse_bh && tid < G) lse_bh[tid] = bad_len ? NAN : -INFINITY;
+        }
+        KVQ_STAMP(5);
+        return;
+    }
+    // a fused append that completes a group quantizes that page itself (split 0) and attends
+    // over it from LDS: the pool supplies only the pages that existed before this call
+    const bool flush = append && L % kGroup == 0;
+    const int full = L / kGroup - (flush ? 1 : 0);      // pages read from the pool
+    const int nres = flush ? kGroup : L % kGroup;       // tokens attended from the residual tile
+    const int n_ps = (full + P - 1) / P;               // splits with pages
+    const int n_work = n_ps > 0 ? n_ps : 1;             // workgroups of this (sequence, KV head)
+    if (split >= n_work) {
+        KVQ_STAMP(5);
+        return;
+    }
+    // the residual tokens belong to split 0: the first workgroups dispatched absorb the extra
+    // work while the last ones are still starting
+    const bool has_res = nres > 0 && split == 0;
+
+    const int pg_end = min(full, (split + 1) * P);
+    const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
     // value pair this lane folds (group a): tokens (w, w+4) of its octet for 8-bit codes,
     // (w%2 + 4*(w/2), +2) for 2- and 4-bit codes, w = r16 % 4 -- the order their B operand
     // pairs take
@@ -704,6 +770,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
     const int t1 = t0 + (VB == 8 ? 4 : 2);
     // powers of two the code unpack leaves on this lane's key channels / value tokens
     const int kshift = unpack_shift<KB>(kj), vshift = unpack_shift<VB>(r16 & 3);
+    // Everything requested so far (the length, the block-table ids, q) is in before the first
+    // page is requested: the memory counter completes in order, so a wait for q issued after
+    // the page requests would also wait for the page.  The q setup below then runs while the
+    // page is in flight.
+    __builtin_amdgcn_s_waitcnt(0);
     const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
     // page ids outside the pool mark the sequence bad (NaN outputs) and are read as page 0
     const bool id_bad = lane < n_my && (my_phys < 0 || my_phys >= p.n_pages);
@@ -713,25 +784,71 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         const int phys = __builtin_amdgcn_readlane(my_phys, j);
         return pool + (static_cast<long long>(phys) * p.H + h) * kPageBytes;
     };
+    // the wave's first page and the residual rows go out as soon as the block-table ids are
+    // in, before the q setup below
     PageRegs<KB, VB> cur, nxt;
     if (n_my > 0) load_page<KB, VB, KM>(cur, page_base(0), lane, ch0, ch1, t0, t1);
     uint4 res_kv[4];
     if (has_res) load_residual(p, bh, nres, append, res_kv);
-    __syncthreads();
-    // per-head normalization exponent: |q * 2^eq| in [1, 2); wave w reduces heads w, w+4, ...
-    for (int hh = wave; hh < G; hh += kWaves) {
-        float mx = fmaxf(fabsf(sm.qs[hh][lane]), fabsf(sm.qs[hh][lane + 64]));
+    KVQ_STAMP(9);
+    // q~ = q log2(e)/sqrt(128); the residual tokens (split 0, after the page loop) read it from
+    // LDS, written here by wave 0
+    if (wave == 0) {
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        if (lane == 0) {
-            int e = 0;
-            if (mx > 0.0f) frexpf(mx, &e);
-            sm.eq[hh] = 1 - e;
+        for (int i = 0; i < GS; ++i) {
+            if (4 * i + a < G) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) sm.qs[4 * i + a][8 * r16 + x] = qbl[i][x] * kScoreScale;
+            }
         }
     }
-    __syncthreads();
+    // per-head normalization exponent eq: |q~ * 2^eq| in [1, 2) -- the maximum over a head's
+    // 128 channels is a 16-lane row maximum of the zero-term layout; every lane of group a
+    // holds it for heads 4i + a, and lane 16*(hh % 4) gives it for any head hh
+    int eqv[GS];
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) mx = fmaxf(mx, fabsf(qbl[i][x]));
+        mx = row_max(mx) * kScoreScale;
+        int e = 0;
+        if (mx > 0.0f) frexpf(mx, &e);
+        eqv[i] = 1 - e;
+    }
+    KVQ_STAMP(10);
 
     const long long slot0 = bh * p.n_splits;
+    int early_cnt = -1;
+    // ---- the split combine's batches of partials (splits s0 .. s0+kCB-1 of this (sequence,
+    // KV head)): one thread per 4 consecutive channels of a head, kMI such items per thread
+    constexpr int kVec = 4, kPerHead = kHeadDim / kVec;
+    constexpr int kMI = (HS * kPerHead + kThreads - 1) / kThreads;     // items per thread
+    constexpr int kCB = 4;
+    float cmv[kMI][kCB], clv[kMI][kCB];
+    float4 cov[kMI][kCB];
+    auto load_batch = [&](int k, int s0) {
+        const int it = tid + k * kThreads;
+        const int hh = min(it / kPerHead, G - 1), c = (it % kPerHead) * kVec;
+        const float *ml_base = p.part_ml + (slot0 * G + hh) * 2;            // split s at + s * G * 2
+        const float *o_base = p.part_o + (slot0 * G + hh) * kHeadDim;       // split s at + s * G * 128
+#pragma unroll
+        for (int jb = 0; jb < kCB; ++jb) {
+            const int s_ = s0 + jb;
+            cmv[k][jb] = -INFINITY;
+            clv[k][jb] = 0.0f;
+            cov[k][jb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (s_ != split && s_ < n_work) {       // this split's own partial comes from registers
+                const float *ml = ml_base + static_cast<long long>(s_) * G * 2;
+                const float *po = o_base + static_cast<long long>(s_) * G * kHeadDim;
+                cmv[k][jb] = load_dev(ml);
+                clv[k][jb] = load_dev(ml + 1);
+                cov[k][jb] = make_float4(load_dev(po + part_slot(c)), load_dev(po + part_slot(c + 1)),
+                                         load_dev(po + part_slot(c + 2)), load_dev(po + part_slot(c + 3)));
+            }
+        }
+    };
+    if (tid == 0) sm.early = 0;
     if (n_ps > 0) {
         WaveLds<GS, KM> &W = sm.u.w[wave];
         constexpr int NP = WaveLds<GS, KM>::NP, PG = WaveLds<GS, KM>::PG;
@@ -761,15 +878,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         float inv_eq[GS];                                       // 2^-eq of the lane's heads
 #pragma unroll
         for (int hh = 0; hh < HS; ++hh) {
-            qw[hh][0] = hh < G ? ldexpf(sm.qs[hh][ch0], sm.eq[hh]) : 0.0f;
-            qw[hh][1] = hh < G ? ldexpf(sm.qs[hh][ch1], sm.eq[hh]) : 0.0f;
+            const int e = __builtin_amdgcn_readlane(eqv[hh / 4], 16 * (hh % 4));
+            qw[hh][0] = hh < G ? ldexpf(qwl[hh][0] * kScoreScale, e) : 0.0f;
+            qw[hh][1] = hh < G ? ldexpf(qwl[hh][1] * kScoreScale, e) : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
             const int hh = 4 * i + a;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) qb[i][x] = hh < G ? ldexpf(sm.qs[hh][8 * r16 + x], sm.eq[hh]) : 0.0f;
-            inv_eq[i] = hh < G ? ldexpf(1.0f, -sm.eq[hh]) : 0.0f;
+            for (int x = 0; x < 8; ++x) qb[i][x] = hh < G ? ldexpf(qbl[i][x] * kScoreScale, eqv[i]) : 0.0f;
+            inv_eq[i] = hh < G ? ldexpf(1.0f, -eqv[i]) : 0.0f;
         }
         // per-token keys: the A operand is q~ itself (page-invariant), folded once; the zero
         // terms need q~ summed over each key group: qsum[i][J] for head 4i + a
@@ -787,8 +905,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                 const int hh = 4 * i + a;
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
-                    const float x = hh < G ? ldexpf(sm.qs[hh][32 * J + 2 * r16] + sm.qs[hh][32 * J + 2 * r16 + 1],
-                                                    sm.eq[hh])
+                    const float x = hh < G ? ldexpf(qtl[i][J][0] * kScoreScale + qtl[i][J][1] * kScoreScale, eqv[i])
                                            : 0.0f;
                     qsum[i][J] = row_sum(x);
                 }
@@ -1080,14 +1197,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         auto prefetch = [&](PageRegs<KB, VB> &dst, int j) {
             load_page<KB, VB, KM>(dst, page_base(min(j, n_my - 1)), lane, ch0, ch1, t0, t1);
         };
+        KVQ_STAMP(1);
         int j = 0;
         for (; j + 1 < n_my; j += 2) {
             prefetch(nxt, j + 1);
             process_page(cur);
+            if (j == 0) KVQ_STAMP(11);
             prefetch(cur, j + 2);
             process_page(nxt);
         }
         if (j < n_my) process_page(cur);
+        KVQ_STAMP(2);
+        // the split counter, read early: used after the merge barrier (see the merge below)
+        if (tid == 0 && n_work > 1) early_cnt = __hip_atomic_load(p.counters + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
         // ---- this wave's state: l per head, value zero terms, unnormalized output -------
         float lw[GS];
@@ -1118,6 +1240,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 #pragma unroll
                 for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(dsum(acc[nb], i), unscale, W.bv[nb >> 1][4 * i + a]);
         }
+        // Thread 0 read the split counter right after its page loop (early_cnt).  When every
+        // other split of this (sequence, KV head) had published its partial by then, this
+        // workgroup combines at once, with its own state from registers, and publishes nothing.
+        if (tid == 0) sm.early = n_work > 1 && early_cnt == n_work - 1;
         __syncthreads();     // every wave is done with its WaveLds: reuse the space
         if (has_res) bad_page |= !residual_tokens<KB, VB, GS, KM>(p, sm, res_kv, nres, G, bh, append, flush, full);
         MergeLds<GS> &M = sm.u.merge;
@@ -1137,18 +1263,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         bad_page |= !residual_tokens<KB, VB, GS, KM>(p, sm, res_kv, nres, G, bh, append, flush, full);
     }
 
-    // ---- this workgroup's merge: its waves' page states and, on the last split, the residual
+    // ---- this workgroup's merge: its waves' page states and, on split 0, the residual ----
     const bool bad = __syncthreads_or(bad_page);
     const bool single = n_work == 1;
+    const bool early = sm.early != 0;
+    // one thread per 4 consecutive channels of a head: the head's weights once, then 16-byte
+    // reads of the waves' partial outputs (exponents <= 0: the raw exp2)
+    float om[kMI], ol[kMI];
+    float4 oo[kMI];
     {
         const MergeLds<GS> &M = sm.u.merge;
-        float *part_o = p.part_o + (slot0 + split) * G * kHeadDim;
-        float *part_ml = p.part_ml + (slot0 + split) * G * 2;
-        // one thread per 4 consecutive channels of a head: the head's weights once, then
-        // 16-byte reads of the waves' partial outputs (exponents <= 0: the raw exp2)
-        constexpr int kVec = 4, kPerHead = kHeadDim / kVec;
-        for (int it = tid; it < G * kPerHead; it += kThreads) {
-            const int hh = it / kPerHead, c = (it % kPerHead) * kVec, idx = hh * kHeadDim + c;
+#pragma unroll
+        for (int k = 0; k < kMI; ++k) {
+            const int it = tid + k * kThreads;
+            om[k] = -INFINITY;
+            ol[k] = 0.0f;
+            oo[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (it >= G * kPerHead) continue;
+            const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
             float m = has_res ? sm.ro.m[hh] : -INFINITY;
             if (n_ps > 0) {
 #pragma unroll
@@ -1171,125 +1303,111 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                     o = make_float4(fmaf(wt, r.x, o.x), fmaf(wt, r.y, o.y), fmaf(wt, r.z, o.z), fmaf(wt, r.w, o.w));
                 }
             }
-            if (single) {
-                const float inv = 1.0f / l;
-                *reinterpret_cast<float4 *>(&out_bh[idx]) =
-                    bad ? make_float4(NAN, NAN, NAN, NAN) : make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-                if (lse_bh && c == 0) lse_bh[hh] = bad ? NAN : (m + log2f(l)) * kLn2;
-            } else {
-                float *po = part_o + hh * kHeadDim;
-                store_dev(po + part_slot(c), bad ? NAN : o.x);
-                store_dev(po + part_slot(c + 1), bad ? NAN : o.y);
-                store_dev(po + part_slot(c + 2), bad ? NAN : o.z);
-                store_dev(po + part_slot(c + 3), bad ? NAN : o.w);
-                if (c == 0) {
-                    store_dev(&part_ml[2 * hh], bad ? 0.0f : m);
-                    store_dev(&part_ml[2 * hh + 1], bad ? NAN : l);
-                }
-            }
+            // a bad sequence: NaN outputs (and a running max that keeps the others' weights finite)
+            om[k] = bad ? 0.0f : m;
+            ol[k] = bad ? NAN : l;
+            oo[k] = bad ? make_float4(NAN, NAN, NAN, NAN) : o;
         }
     }
-    if (single) return;
-    wait_stores();
-    __syncthreads();
-    if (tid == 0)
-        sm.last = __hip_atomic_fetch_add(p.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_work - 1;
-    __syncthreads();
-    if (!sm.last) return;
-
-    // ---- the last workgroup of this (sequence, KV head) to finish merges every split.
-    // (m, l) of a chunk of splits is staged in LDS; the o partials are read in batches of 8
-    // splits whose loads are all issued before any is used (device-scope loads go past the
-    // L2, so a dependent chain of them would cost one memory round trip per split).
-    constexpr int kItems = (HS * kHeadDim + kThreads - 1) / kThreads;
-    constexpr int kPer = kMergeChunk * 16 / kThreads;
-    constexpr int kBatch = 8;
-    CombineLds &C = sm.u.comb;
-    float mx[kItems], ls[kItems], os[kItems];
+    if (single) {
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-        mx[it] = -INFINITY;
-        ls[it] = 0.0f;
-        os[it] = 0.0f;
+        for (int k = 0; k < kMI; ++k) {
+            const int it = tid + k * kThreads;
+            if (it >= G * kPerHead) continue;
+            const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
+            const float inv = 1.0f / ol[k];
+            *reinterpret_cast<float4 *>(&out_bh[hh * kHeadDim + c]) =
+                make_float4(oo[k].x * inv, oo[k].y * inv, oo[k].z * inv, oo[k].w * inv);
+            if (lse_bh && c == 0) lse_bh[hh] = (om[k] + log2f(ol[k])) * kLn2;
+        }
+        KVQ_STAMP(3);
+        KVQ_STAMP(5);
+        return;
     }
-    for (int c0 = 0; c0 < n_work; c0 += kMergeChunk) {
-        const int cnt = min(kMergeChunk, n_work - c0);
-        float x[kItems][kBatch];
-        auto load_o = [&](int s0) {
+    if (!early) {
+        // publish (m, l, o) with device-scope stores, wait until they are complete, then count
+        // this split in; the workgroup that completes the count combines
 #pragma unroll
-            for (int it = 0; it < kItems; ++it) {
-                const int idx = tid + it * kThreads;
-                const int g = idx / kHeadDim, c = idx % kHeadDim;
+        for (int k = 0; k < kMI; ++k) {
+            const int it = tid + k * kThreads;
+            if (it >= G * kPerHead) continue;
+            const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
+            float *po = p.part_o + ((slot0 + split) * G + hh) * kHeadDim;
+            store_dev(po + part_slot(c), oo[k].x);
+            store_dev(po + part_slot(c + 1), oo[k].y);
+            store_dev(po + part_slot(c + 2), oo[k].z);
+            store_dev(po + part_slot(c + 3), oo[k].w);
+            if (c == 0) {
+                float *pml = p.part_ml + ((slot0 + split) * G + hh) * 2;
+                store_dev(pml, om[k]);
+                store_dev(pml + 1, ol[k]);
+            }
+        }
+        KVQ_STAMP(3);
+        wait_stores();
+        __syncthreads();
+        if (tid == 0)
+            sm.last = __hip_atomic_fetch_add(p.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_work - 1;
+        __syncthreads();
+        KVQ_STAMP(4);
+        if (!sm.last) {
+            KVQ_STAMP(5);
+            return;
+        }
+    } else {
+        KVQ_STAMP(3);
+        KVQ_STAMP(4);
+    }
+
+    // ---- combine every split of this (sequence, KV head): the maximum over all running maxima,
+    // then the weighted sums in split order, so the result does not depend on which workgroup
+    // combines.  Other splits' partials are read with device-scope loads issued in batches of
+    // kCB splits (a dependent chain would cost one memory round trip per split); this split's
+    // own partial comes from registers.
 #pragma unroll
-                for (int k = 0; k < kBatch; ++k)
-                    x[it][k] = (idx < G * kHeadDim && s0 + k < cnt)
-                                   ? load_dev(p.part_o + ((slot0 + c0 + s0 + k) * G + g) * kHeadDim + part_slot(c))
-                                   : 0.0f;
+    for (int k = 0; k < kMI; ++k) {
+        const int it = tid + k * kThreads;
+        if (it >= G * kPerHead) continue;
+        const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
+        const float *ml_base = p.part_ml + (slot0 * G + hh) * 2;
+        load_batch(k, 0);
+        auto own = [&](int s0) {
+            if (split >= s0 && split < s0 + kCB) {
+                cmv[k][split - s0] = om[k];
+                clv[k][split - s0] = ol[k];
+                cov[k][split - s0] = oo[k];
             }
         };
-        float mv[kPer], lv[kPer];
+        own(0);
+        float mx = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int i = tid + k * kThreads;
-            if (i < cnt * G) {
-                const float *src = p.part_ml + ((slot0 + c0 + i / G) * G + i % G) * 2;
-                mv[k] = load_dev(src);
-                lv[k] = load_dev(src + 1);
-            }
-        }
-        load_o(0);      // in flight together with the (m, l) loads
+        for (int jb = 0; jb < kCB; ++jb) mx = fmaxf(mx, cmv[k][jb]);
+        for (int s_ = kCB; s_ < n_work; ++s_)
+            mx = fmaxf(mx, s_ == split ? om[k] : load_dev(ml_base + static_cast<long long>(s_) * G * 2));
+        float l = 0.0f;
+        float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int s0 = 0;;) {
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int i = tid + k * kThreads;
-            if (i < cnt * G) {
-                C.m[i / G][i % G] = mv[k];
-                C.l[i / G][i % G] = lv[k];
-            }
-        }
-        __syncthreads();
-        float mn[kItems];
-#pragma unroll
-        for (int it = 0; it < kItems; ++it) {
-            const int idx = tid + it * kThreads;
-            const int g = idx / kHeadDim;
-            float mc = -INFINITY;
-            if (idx < G * kHeadDim)
-                for (int s2 = 0; s2 < cnt; ++s2) mc = fmaxf(mc, C.m[s2][g]);
-            mn[it] = fmaxf(mx[it], mc);
-            const float sc = mx[it] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mx[it] - mn[it]);
-            ls[it] *= sc;
-            os[it] *= sc;
-            mx[it] = mn[it];
-        }
-        for (int s0 = 0; s0 < cnt; s0 += kBatch) {
-            if (s0 > 0) load_o(s0);
-#pragma unroll
-            for (int it = 0; it < kItems; ++it) {
-                const int idx = tid + it * kThreads;
-                const int g = idx / kHeadDim;
-                if (idx < G * kHeadDim) {
-#pragma unroll
-                    for (int k = 0; k < kBatch; ++k) {
-                        if (s0 + k < cnt) {
-                            const float w = __builtin_amdgcn_exp2f(C.m[s0 + k][g] - mn[it]);
-                            ls[it] = fmaf(w, C.l[s0 + k][g], ls[it]);
-                            os[it] = fmaf(w, x[it][k], os[it]);
-                        }
-                    }
+            for (int jb = 0; jb < kCB; ++jb) {
+                if (s0 + jb < n_work) {
+                    const float w = cmv[k][jb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(cmv[k][jb] - mx);
+                    l = fmaf(w, clv[k][jb], l);
+                    o = make_float4(fmaf(w, cov[k][jb].x, o.x), fmaf(w, cov[k][jb].y, o.y), fmaf(w, cov[k][jb].z, o.z),
+                                    fmaf(w, cov[k][jb].w, o.w));
                 }
             }
+            s0 += kCB;
+            if (s0 >= n_work) break;
+            load_batch(k, s0);
+            own(s0);
         }
-        __syncthreads();
+        const float inv = 1.0f / l;
+        *reinterpret_cast<float4 *>(&out_bh[hh * kHeadDim + c]) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        if (lse_bh && c == 0) lse_bh[hh] = (mx + log2f(l)) * kLn2;
     }
-#pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-        const int idx = tid + it * kThreads;
-        if (idx < G * kHeadDim) {
-            out_bh[idx] = os[it] / ls[it];
-            if (lse_bh && idx % kHeadDim == 0) lse_bh[idx / kHeadDim] = (mx[it] + log2f(ls[it])) * kLn2;
-        }
-    }
+    // the count is complete (or was, for an early combine): reset it for the next call
     if (tid == 0) __hip_atomic_store(p.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    KVQ_STAMP(5);
 }
 
 #if defined(KVQ_DECODE_COMMON)

@@ -61,7 +61,22 @@ struct DecodeParams {
     int max_seq_len;
     int pages_per_split;
     int n_splits;         // page splits per (b, h)
+    // profiling build only (KVQ_PHASE_TIMERS): per wave, [kPhaseStamps] u64 real-time
+    // stamps at the kernel's phase boundaries; null otherwise
+    unsigned long long *phase_ts;
 };
+
+// Phase-timer record per wave (KVQ_PHASE_TIMERS builds): stamps 0-5 are the 100 MHz
+// real-time counter at entry, page loop start, page loop end, partials stored, split
+// counter known, exit; stamps 8-13 at finer points: length known, q staged (first barrier),
+// q exponents (second barrier), first page done, residual tokens start and end (0 where
+// a wave did not reach the point).  Stamp 6 holds the hardware XCC id (bits 32-35) and
+// HW_ID register (bits 0-31); stamp 7 the work item as h | b << 20 | split << 40.
+constexpr int kPhaseStamps = 16;
+#if defined(KVQ_PHASE_TIMERS)
+extern unsigned long long *g_phase_buf;   // set by kvq_profile_set_phase_buffer (profiling build)
+extern size_t g_phase_bytes;
+#endif
 
 // Workspace layout of kvq_decode_attn for (batch, H, G, n_splits).
 struct DecodeWorkspace {
@@ -83,3 +98,10 @@ hipError_t launch_decode_kb16(int vb, int kmode, const DecodeParams &p, bool q_f
 hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t s);
 
 }  // namespace kvq
+
+#if defined(KVQ_PHASE_TIMERS)
+// Profiling build only (libkvq_phases.so): every later decode launch whose per-wave
+// records ([H][batch][splits][4 waves][kPhaseStamps] u64) fit in `bytes` writes them to
+// the device buffer `buf`; null turns the recording off.
+extern "C" void kvq_profile_set_phase_buffer(void *buf, size_t bytes);
+#endif

@@ -6,6 +6,14 @@
            --fetch <csv> --write <csv> --copy-fetch <csv> --copy-write <csv> --copy-bytes N
            --alg-bytes-per-launch A --source <file.hip> --out <json>
 
+    python -m layer_wise_mixed_kvq_amd.profiling phases [--config llama] [--layer 3] [--out F]
+
+`phases` (needs the profiling build, `python -m layer_wise_mixed_kvq_amd.build
+--phase-timers`) replays a benchmark decode step as a graph in which one layer's launch
+records, per wave, the 100 MHz real-time counter at the decode kernel's phase boundaries,
+and prints when each phase ends across the launch's waves (relative to its first wave's
+entry) and how the work items sat on the XCDs.
+
 `traffic` turns the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) into HBM bytes per
 launch: each counter is scaled by what it reads for a plain copy kernel of known size
 (the copy reads N bytes and writes N bytes), so both the KiB unit and any systematic
@@ -131,6 +139,134 @@ def traffic_md(rec: dict) -> str:
     return "\n".join(lines) + "\n"
 
 
+PHASE_NAMES = {0: "entry", 8: "length known", 9: "q staged (barrier 1)", 10: "q exponents (barrier 2)",
+               1: "page loop start", 11: "first page done", 2: "page loop end", 12: "residual start",
+               13: "residual end", 3: "partials stored", 4: "split counter known", 5: "exit"}
+N_STAMPS = 16
+
+
+def phase_summary(rec) -> dict:
+    """Summary of one launch's phase records: numpy uint64 [n_waves][N_STAMPS] (see kPhaseStamps
+    in csrc/kvq_internal.h)."""
+    import numpy as np
+    live = rec[rec[:, 0] != 0]
+    t0 = live[:, 0].min()
+    rel = lambda col: (live[:, col].astype(np.int64) - int(t0)) * 10.0 / 1000.0   # us (10 ns ticks)
+    out = {"waves": int(len(live)), "phases": {}}
+    for k, name in PHASE_NAMES.items():
+        sel = live[:, k] != 0
+        if not sel.any():
+            continue
+        v = rel(k)[sel]
+        out["phases"][name] = {"waves": int(sel.sum()), "min_us": float(v.min()), "median_us": float(np.median(v)),
+                               "p90_us": float(np.percentile(v, 90)), "max_us": float(v.max())}
+    # per-wave durations of the page loop, the merge and the combine
+    dur = {}
+    for a, b, name in ((1, 2, "page loop"), (2, 3, "merge + partial stores"), (3, 4, "store wait + counter"),
+                       (4, 5, "after the counter (combine on the last workgroup)"), (0, 1, "prologue")):
+        sel = (live[:, a] != 0) & (live[:, b] != 0)
+        if sel.any():
+            d = (live[sel, b].astype(np.int64) - live[sel, a].astype(np.int64)) * 0.01
+            dur[name] = {"median_us": float(np.median(d)), "max_us": float(d.max())}
+    out["durations"] = dur
+    # page loop end by split index (early- and late-dispatched halves)
+    split = (live[:, 7] >> 40).astype(np.int64)
+    sel = live[:, 2] != 0
+    if sel.any():
+        by = {}
+        for sp in np.unique(split[sel]):
+            v = rel(2)[sel & (split == sp)]
+            by[int(sp)] = float(np.median(v))
+        out["page_loop_end_median_by_split_us"] = by
+    # XCD placement: does every (sequence, KV head) keep all its splits on one XCD?
+    xcc = ((live[:, 6] >> 32) & 0xF).astype(np.int64)
+    item = (live[:, 7] & ((1 << 40) - 1)).astype(np.int64)
+    one = all(len(np.unique(xcc[item == it])) == 1 for it in np.unique(item))
+    out["xcds"] = {"waves_per_xcd": {int(x): int((xcc == x).sum()) for x in np.unique(xcc)},
+                   "every_item_on_one_xcd": bool(one)}
+    return out
+
+
+def phases_md(summ: dict, cmd: str, title: str) -> str:
+    lines = [f"# Decode kernel phase timers: {title}", "", f"Command: `{cmd}`", "",
+             "Per-wave stamps of the 100 MHz real-time counter (10 ns ticks), relative to the first wave's entry "
+             f"into the launch; {summ['waves']} waves.", "",
+             "| phase boundary | waves | min us | median us | p90 us | max us |", "|---|---|---|---|---|---|"]
+    for name, v in summ["phases"].items():
+        lines.append(f"| {name} | {v['waves']} | {v['min_us']:.2f} | {v['median_us']:.2f} | {v['p90_us']:.2f} | "
+                     f"{v['max_us']:.2f} |")
+    lines += ["", "| per-wave duration | median us | max us |", "|---|---|---|"]
+    for name, v in summ["durations"].items():
+        lines.append(f"| {name} | {v['median_us']:.2f} | {v['max_us']:.2f} |")
+    if "page_loop_end_median_by_split_us" in summ:
+        lines += ["", "Page loop end, median by split index (us): " +
+                  ", ".join(f"{k}: {v:.2f}" for k, v in summ["page_loop_end_median_by_split_us"].items())]
+    x = summ["xcds"]
+    lines += ["", "Waves per XCD: " + ", ".join(f"{k}: {v}" for k, v in x["waves_per_xcd"].items()) +
+              f"; every (sequence, KV head) on one XCD: {x['every_item_on_one_xcd']}"]
+    return "\n".join(lines) + "\n"
+
+
+def phases(args) -> str:
+    import os
+    import numpy as np
+    import torch
+    from . import _native
+    _native.use_phase_timer_build(args.lib)
+    from . import _native as nat
+    L = nat.lib()
+    if not hasattr(L, "kvq_profile_set_phase_buffer"):
+        raise SystemExit("libkvq_phases.so lacks the phase timers: build it with "
+                         "python -m layer_wise_mixed_kvq_amd.build --phase-timers")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    cfg = bench.CONFIGS[args.config]
+    stack = bench.DecodeStack(cfg, "cuda")
+    n_rec = stack.H * stack.B * stack.max_pages * 4
+    buf = torch.zeros(n_rec * N_STAMPS, dtype=torch.int64, device="cuda")
+    kvq = stack.kvq
+
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def step():
+        for l in range(len(stack.caches)):
+            if l == args.layer and args.touch_stride:
+                # read one byte per touch_stride bytes of the layer's buffers just before its
+                # launch (address translations warm, almost no data cached)
+                c = stack.caches[l]
+                for t in (c.pages.view(-1), stack.q[l].view(torch.uint8).view(-1), stack.out[l].view(torch.uint8).view(-1)):
+                    sink.add_(t[::args.touch_stride].sum())
+            if l == args.layer:
+                L.kvq_profile_set_phase_buffer(buf.data_ptr(), buf.numel() * 8)
+            kvq.kvq_append_decode_attn(stack.model, l, stack.caches[l], stack.k_new[l], stack.v_new[l], stack.pos,
+                                       stack.q[l], stack.L, out=stack.out[l], lse=stack.lse[l],
+                                       workspace=stack.workspace)
+            if l == args.layer:
+                L.kvq_profile_set_phase_buffer(None, 0)
+
+    g = bench.capture(step)
+    summaries = []
+    for r in range(args.reps):
+        buf.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        rec = buf.view(-1, N_STAMPS).cpu().numpy().view(np.uint64)
+        summaries.append(phase_summary(rec))
+    # the replay with the median exit time
+    summaries.sort(key=lambda s_: s_["phases"]["exit"]["max_us"])
+    summ = summaries[len(summaries) // 2]
+    kb, vb = cfg["pairs"][args.layer] if not isinstance(cfg["pairs"][args.layer], str) else (0, 0)
+    title = (f"{cfg['workload']}, layer {args.layer} ({cfg['pairs'][args.layer]}); median of {args.reps} graph "
+             "replays of the whole step by last exit")
+    text = phases_md(summ, args.cmd or " ".join(sys.argv), title)
+    summ["exit_max_us_all_replays"] = [s_["phases"]["exit"]["max_us"] for s_ in summaries]
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(summ, f, indent=1)
+    return text
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m layer_wise_mixed_kvq_amd.profiling")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -157,11 +293,23 @@ def main(argv=None):
     t.add_argument("--cmd", action="append")
     t.add_argument("--out", required=True, help="JSON record; a .md summary is written beside it")
     t.add_argument("--md")
+    ph = sub.add_parser("phases")
+    ph.add_argument("--config", default="llama")
+    ph.add_argument("--layer", type=int, default=3)
+    ph.add_argument("--reps", type=int, default=7)
+    ph.add_argument("--cmd")
+    ph.add_argument("--json")
+    ph.add_argument("--lib", help="another phase-timer build of the library to load")
+    ph.add_argument("--touch-stride", type=int, default=0,
+                    help="before the layer's launch, read one byte per this many bytes of its pool, q and out")
+    ph.add_argument("--out")
     a = ap.parse_args(argv)
     if a.what == "stats":
         text = stats_md(a.csv, a.cmd)
     elif a.what == "pmc":
         text = pmc_md(a.csv, a.cmd, a.kernel_regex)
+    elif a.what == "phases":
+        text = phases(a)
     else:
         rec = traffic(a)
         with open(a.out, "w") as f:

@@ -508,7 +508,7 @@ int orc_pack_x(int kb, int vb, int fmt, const float *scales, int H, int batch, i
 {
     if (!valid_format(kb, vb, fmt)) return 1;
     const size_t hp = orc_head_page_bytes_x(kb, vb, fmt);
-    static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
+    float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];   /* per call: the oracle is called from several threads */
     for (int b = 0; b < batch; ++b) {
         int L = seq_len[b];
         if (L < 0 || L > max_tokens || L > 32 * max_pages) return 2;
@@ -547,7 +547,7 @@ int orc_append_x(int kb, int vb, int fmt, const float *scales, int H, int batch,
 {
     if (!valid_format(kb, vb, fmt)) return 1;
     const size_t hp = orc_head_page_bytes_x(kb, vb, fmt);
-    static float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];
+    float tk[ORC_G * ORC_D], tv[ORC_G * ORC_D];   /* per call: the oracle is called from several threads */
     for (int b = 0; b < batch; ++b) {
         int p = pos[b];
         if (p < 0 || p >= 32 * max_pages) return 2;

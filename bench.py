@@ -60,7 +60,7 @@ CONFIGS = {
                  seed=20250205),
     "single": dict(workload="single layer K8V4, GQA 4, 512 tokens, fp32 K/V/q (attention only)",
                    pairs=[(8, 4)], n_q_heads=4, n_kv_heads=1, batch=1, context=512, n_outliers=4,
-                   seed=2024, f32=True),
+                   seed=2024, f32=True, append=False),
     "ragged": dict(workload="llama3.1-8b-shape C3.25 paged decode step, batch 256, lengths U{1024..32768}, "
                             "shuffled page pool (append + attention, 32 layers)",
                    pairs=LLAMA_C325, n_q_heads=32, n_kv_heads=8, batch=256, ragged=(1024, 32768), shuffle=True,
@@ -171,7 +171,10 @@ class DecodeStack:
             lens = np.full(B, cfg["context"], dtype=np.int64)
         self.lens = lens
         self.B, self.H, self.Hq, self.C = B, H, cfg["n_q_heads"], int(lens.max())
-        self.L = self.C + 1
+        # a decode step appends token C and attends over C + 1 tokens; the single-layer
+        # workload attends over exactly its C given tokens
+        self.extra = 1 if cfg.get("append", True) else 0
+        self.L = self.C + self.extra
         n_log = (lens + 1 + 31) // 32                      # pages incl. room for the appended token
         self.max_pages = int(n_log.max())
         n_phys = int(n_log.sum())
@@ -216,7 +219,7 @@ class DecodeStack:
         torch.cuda.synchronize()
         del order
         self.pos = torch.from_numpy(lens.astype(np.int32)).to(device)
-        self.attend = lens + 1
+        self.attend = lens + self.extra
         self.seq_len = torch.from_numpy(self.attend.astype(np.int32)).to(device)
         self.workspace = kvq.new_workspace(self.model, B, self.L, 0, device)
 
@@ -369,38 +372,283 @@ def quality_report(stack, n_seq=4):
     return {"sequences": nb, "reference": "fp32 attention over the unquantized source tokens", "layers": rep}
 
 
-def cpu_baseline_decode(cfg, stack, n_seq):
-    """The CPU oracle, as it stands (single thread), on the batch's first `n_seq` sequences
-    for every layer: the same append + attention work of one decode step.  Packing the
-    sample (prefill) is not timed.  Returns (seconds, tokens attended in the sample)."""
+def host_info():
+    """nproc and the CPU model string of the host the oracle runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+class OneCore:
+    """While the oracle is timed, the calling thread runs on one core only (the lowest-numbered
+    core it may use); the previous affinity is restored afterwards."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.core = min(self.saved)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+
+
+def _bits16(t):
     import numpy as np
     import torch
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def oracle_decode_seq(cfg, l, b, C, append=True):
+    """Seconds the oracle takes for sequence b of layer l at C cached tokens: the append of the
+    new token (when `append`) and binary64 attention over C (+1) tokens; packing the sequence
+    beforehand is not timed."""
+    import numpy as np
     import oracle as orc
     import synth
     seed, H, Hq = cfg["seed"], cfg["n_kv_heads"], cfg["n_q_heads"]
-    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
-    t_total, attended = 0.0, 0
-    for l, entry in enumerate(cfg["pairs"]):
-        kb, vb, km, _ = layer_spec(entry, cfg.get("k_mode", 0))
-        scales = np.array([FP8_SCALES] * H, dtype=np.float32) if km == 2 else None
-        cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
-        for b in range(n_seq):
-            C = int(stack.lens[b])
-            maxp = (C + 1 + 31) // 32
-            bt = np.arange(maxp, dtype=np.int32).reshape(1, maxp)
-            k = synth.fill(seed, synth.KIND_K, l, 1, C, H, b0=b, chan_mult=cm)
-            v = synth.fill(seed, synth.KIND_V, l, 1, C, H, b0=b)
-            kn = synth.fill(seed, synth.KIND_K_NEW, l, 1, 1, H, b0=b, chan_mult=cm).view(1, H, 128)
-            vn = synth.fill(seed, synth.KIND_V_NEW, l, 1, 1, H, b0=b).view(1, H, 128)
-            q = synth.fill(seed, synth.KIND_Q, l, 1, 1, Hq, b0=b).view(1, Hq, 128)
-            pages, rk, rv = orc.new_cache(kb, vb, H, 1, maxp, km)
-            orc.pack(kb, vb, bits(k), bits(v), [C], bt, pages, rk, rv, kmode=km, scales=scales)
-            t0 = time.perf_counter()
-            orc.append(kb, vb, bits(kn), bits(vn), [C], bt, pages, rk, rv, kmode=km, scales=scales)
-            orc.decode_attn(kb, vb, H, bits(q), [C + 1], bt, pages, rk, rv, kmode=km, scales=scales)
-            t_total += time.perf_counter() - t0
-            attended += C + 1
-    return t_total, attended
+    kb, vb, km, _ = layer_spec(cfg["pairs"][l], cfg.get("k_mode", 0))
+    scales = np.array([FP8_SCALES] * H, dtype=np.float32) if km == 2 else None
+    cm = synth.outlier_mult(seed, l, H, cfg["n_outliers"])
+    f32 = cfg.get("f32", False)
+    dt = "f32" if f32 else "bf16"
+    conv = (lambda t: t.contiguous().numpy()) if f32 else _bits16
+    maxp = (C + 1 + 31) // 32
+    bt = np.arange(maxp, dtype=np.int32).reshape(1, maxp)
+    k = synth.fill(seed, synth.KIND_K, l, 1, C, H, b0=b, chan_mult=cm, dtype=dt)
+    v = synth.fill(seed, synth.KIND_V, l, 1, C, H, b0=b, dtype=dt)
+    q = synth.fill(seed, synth.KIND_Q, l, 1, 1, Hq, b0=b, dtype=dt).view(1, Hq, 128)
+    pages, rk, rv = orc.new_cache(kb, vb, H, 1, maxp, km)
+    orc.pack(kb, vb, conv(k), conv(v), [C], bt, pages, rk, rv, kmode=km, scales=scales)
+    if append:
+        kn = synth.fill(seed, synth.KIND_K_NEW, l, 1, 1, H, b0=b, chan_mult=cm).view(1, H, 128)
+        vn = synth.fill(seed, synth.KIND_V_NEW, l, 1, 1, H, b0=b).view(1, H, 128)
+    t0 = time.perf_counter()
+    if append:
+        orc.append(kb, vb, _bits16(kn), _bits16(vn), [C], bt, pages, rk, rv, kmode=km, scales=scales)
+    orc.decode_attn(kb, vb, H, conv(q), [C + (1 if append else 0)], bt, pages, rk, rv, kmode=km, scales=scales)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_decode(cfg, lens, seqs, layers=None, append=True):
+    """The CPU oracle as it stands, on one core: append + attention of sequences `seqs` for
+    `layers` (default: every layer).  Returns {layer: [seconds per sequence]}."""
+    layers = range(len(cfg["pairs"])) if layers is None else layers
+    out = {}
+    with OneCore():
+        for l in layers:
+            out[l] = [oracle_decode_seq(cfg, l, b, int(lens[b]), append) for b in seqs]
+    return out
+
+
+def cpu_record(value, unit, sample, extrapolated=False):
+    return dict({"value": value, "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
+                 "extrapolated": extrapolated}, **host_info())
+
+
+def cpu_baseline_for(name, cfg, stack):
+    """The oracle's rate on a bounded sample of workload `name` (about 10-30 s of one core)."""
+    import numpy as np
+    lens = stack.lens
+    n_layers = len(cfg["pairs"])
+    if name == "single":
+        t = cpu_baseline_decode(cfg, lens, [0], append=False)
+        secs = sum(v[0] for v in t.values())
+        return cpu_record(1.0 / secs, "tokens/s", "the whole workload: binary64 attention of the one query over "
+                          "its 512 tokens (packing not timed)")
+    if name in ("llama", "ktoken", "bf16fp8"):
+        seqs = list(range(min(5, stack.B)))
+        t = cpu_baseline_decode(cfg, lens, seqs)
+        secs = sum(sum(v) for v in t.values())
+        return cpu_record(len(seqs) / secs, "tokens/s",
+                          f"{len(seqs)} of {stack.B} sequences, all {n_layers} layers: append + binary64 attention "
+                          "(packing of the sample not timed)")
+    if name == "qwen":
+        t = cpu_baseline_decode(cfg, lens, [0])
+        secs = sum(v[0] for v in t.values())
+        return cpu_record(1.0 / secs, "tokens/s",
+                          f"1 of {stack.B} sequences, all {n_layers} layers: append + binary64 attention "
+                          "(packing of the sample not timed)")
+    if name == "ragged":
+        # the shortest and the longest sequence, one whose append flushes a page, one more; one
+        # layer of each distinct pair; seconds per attended token of each pair, extrapolated to
+        # every sequence and layer by attended tokens
+        flush = int(np.nonzero(lens % 32 == 31)[0][0]) if np.any(lens % 32 == 31) else 1
+        seqs = [int(np.argmin(lens)), int(np.argmax(lens)), flush, 100 % stack.B]
+        first = {}
+        for l, e in enumerate(cfg["pairs"]):
+            first.setdefault(tuple(e) if not isinstance(e, str) else e, l)
+        t = cpu_baseline_decode(cfg, lens, seqs, layers=sorted(first.values()))
+        attended = sum(int(lens[b]) + 1 for b in seqs)
+        per_tok = {l: sum(v) / attended for l, v in t.items()}
+        total_tok = int((lens + 1).sum())
+        est = sum(per_tok[first[tuple(e) if not isinstance(e, str) else e]] * total_tok for e in cfg["pairs"])
+        return cpu_record(stack.B / est, "tokens/s",
+                          f"sequences {seqs} (shortest, longest, one that flushes, one more) at layers "
+                          f"{sorted(first.values())} (one per distinct pair); step time extrapolated to all "
+                          f"{stack.B} sequences and {n_layers} layers by attended tokens ({est:.1f} s per step)",
+                          extrapolated=True)
+    return None
+
+
+def decode_workload(name, args, dev, flush_step=False):
+    """Time one decode workload as the headline does: the fused append + attention step over
+    every layer, captured as a graph.  Returns the record (not printed)."""
+    import torch
+    import layer_wise_mixed_kvq_amd as kvq
+    cfg = CONFIGS[name]
+    log(f"[bench] building {name} cache ...")
+    t0 = time.perf_counter()
+    stack = DecodeStack(cfg, dev)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    log(f"[bench] cache built in {build_s:.1f} s")
+    with_append = cfg.get("append", True)
+    step_fn = (lambda: stack.step(with_append, fused=not args.unfused))
+    if args.no_graph:
+        for _ in range(args.warmup):
+            step_fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            step_fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms, wall = e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
+        step_stats = None
+    else:
+        g = capture(step_fn)
+        log("[bench] graph captured; timing")
+        ms, wall = time_graph(g, args.steps, args.warmup)
+        step_stats = replay_stats(g, 20)
+        del g
+    # attention-only step, and the step with the append as its own launch (context)
+    g_attn = capture(lambda: stack.step(False))
+    ms_attn, _ = time_graph(g_attn, args.steps, 2)
+    del g_attn
+    ms_unfused = None
+    if with_append and not args.unfused:
+        g_unf = capture(lambda: stack.step(True, fused=False))
+        ms_unfused, _ = time_graph(g_unf, args.steps, 2)
+        del g_unf
+    log(f"[bench] {name}: step {ms:.4f} ms (attention only {ms_attn:.4f} ms, append as its own launch "
+        f"{ms_unfused} ms)")
+    # the dominant kernel (decode attention): its average launch duration is the
+    # attention-only step (one launch per layer, replayed as a graph on the stream the kernels
+    # run on, timed with events over the whole timed region) divided by the layer count;
+    # event pairs around single eager launches are reported beside it (they add a few us of
+    # marker overhead per launch)
+    n_layers = len(cfg["pairs"])
+    dbytes = stack.decode_bytes()
+    launch_us = ms_attn * 1e3 / n_layers
+    achieved = sum(dbytes) / (ms_attn * 1e-3) / 1e9
+    durs = per_launch_durations(stack.decode_layer, n_layers, args.roofline_reps)
+    log(f"[bench] {name}: decode kernel avg {launch_us:.2f} us/launch (graph), "
+        f"{sum(durs) / n_layers * 1e3:.2f} us (eager, event pairs); {achieved:.1f} GB/s")
+    step_bytes = stack.alg_bytes(with_append)
+    quality = quality_report(stack) if (with_append and args.quality) else None
+    if quality:
+        for qn, r in quality["layers"].items():
+            log(f"[bench] {qn} (layer {r['layer']}): K rel RMS {r['k_rel_rms']:.4f}, V {r['v_rel_rms']:.4f}; "
+                f"attention vs fp32 max abs {r['attn_max_abs_vs_fp32']:.2e}, rel RMS {r['attn_rel_rms_vs_fp32']:.4f}")
+    flush = None
+    if flush_step and with_append:
+        flush = flush_step_timing(cfg, args, dev, ms, stack)
+    lens = stack.lens
+    B = stack.B
+    rec = {
+        "metric": "mixed-precision KV decode-attn tokens/s + packed-KV GB/s (% HBM peak), 1 GPU",
+        "value": B * 1000.0 / ms,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": stack_dtype(stack),
+        "data": "synthetic (seeded Irwin-Hall N(0,1) K/V/q, outlier key channels x10 per layer and head)",
+        "config": {"workload": cfg["workload"], "batch": B, "context": stack.C,
+                   "attended_tokens": stack.L, "mean_attended_tokens": float(stack.attend.mean()), "layers": n_layers,
+                   "n_q_heads": stack.Hq, "n_kv_heads": stack.H, "head_dim": 128,
+                   "equiv_bits": kvq.kvq_equiv_bits(stack.model), "graph": not args.no_graph,
+                   "fused_append": with_append and not args.unfused,
+                   "keys": "per-token" if stack.k_mode else "per-channel"},
+        "packed_kv_gbps": step_bytes / (ms * 1e-3) / 1e9,
+        "packed_kv_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "step_alg_bytes": step_bytes,
+        "attention_only_ms_per_step": ms_attn,
+        "unfused_append_ms_per_step": ms_unfused,
+        "wall_s_timed": wall,
+        "step_ms_median_min": step_stats,
+        "cache_build_s": build_s,
+        "flush_step": flush,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(name),
+                     "kernel": "decode_kernel (kvq_decode_attn)",
+                     "avg_launch_us": launch_us,
+                     "avg_launch_us_eager_events": sum(durs) / n_layers * 1e3,
+                     "alg_bytes_per_launch": sum(dbytes) / n_layers},
+        "cpu_baseline": None,
+        "quantization_error": quality,
+    }
+    del stack
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if args.cpu_baseline:
+        log(f"[bench] {name}: CPU oracle baseline ...")
+        t0 = time.perf_counter()
+        rec["cpu_baseline"] = cpu_baseline_for(name, cfg, _LensOnly(lens, B))
+        log(f"[bench] {name}: CPU oracle {rec['cpu_baseline']['value']:.4g} {rec['cpu_baseline']['unit']} "
+            f"({time.perf_counter() - t0:.1f} s)")
+    return rec
+
+
+class _LensOnly:
+    """The sequence lengths and batch of a workload (what the oracle sample needs)."""
+
+    def __init__(self, lens, B):
+        self.lens, self.B = lens, B
+
+
+def flush_step_timing(cfg, args, dev, ms_steady, stack_steady):
+    """A decode step in which every sequence's appended token completes a page (one token
+    short of a page boundary): the fused launch quantizes that page and attends over it.  One
+    step in 32 is such a step, so the amortized rate is batch * 32 / (31 * steady + flush)."""
+    import torch
+    C = int(stack_steady.lens.max())
+    ctx = (C // 32) * 32 - 1
+    fstack = DecodeStack(dict(cfg, context=ctx), dev)
+    g = capture(lambda: fstack.step(True))
+    ms_flush, _ = time_graph(g, args.steps, args.warmup)
+    del g
+    g_attn = capture(lambda: fstack.step(False))
+    ms_flush_attn, _ = time_graph(g_attn, args.steps, 2)
+    del g_attn
+    B, n_layers = fstack.B, len(cfg["pairs"])
+    del fstack
+    torch.cuda.empty_cache()
+    amort = B * 32 * 1000.0 / (31 * ms_steady + ms_flush)
+    log(f"[bench] flush step ({ctx} cached tokens, every append completes a page): {ms_flush:.4f} ms "
+        f"(attention only {ms_flush_attn:.4f} ms); 32-step amortized {amort:.0f} tokens/s")
+    return {"context": ctx, "ms_per_step": ms_flush, "attention_only_ms_per_step": ms_flush_attn,
+            "flush_cost_us_per_launch": (ms_flush - ms_flush_attn) * 1e3 / n_layers,
+            "tokens_per_s_flush_step": B * 1000.0 / ms_flush,
+            "tokens_per_s_32_step_amortized": amort}
+
+
+def pack_workload(args, dev):
+    return bench_pack(CONFIGS["pack"], args, emit=False)
 
 
 def main():
@@ -410,7 +658,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama", choices=sorted(CONFIGS))
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
-    ap.add_argument("--cpu-seqs", type=int, default=5, help="sequences in the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false",
+                    help="skip the oracle's CPU baseline legs")
+    ap.add_argument("--no-quality", dest="quality", action="store_false",
+                    help="skip the quantization-error report")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="with the default workload: skip the nested records of the other workloads")
     ap.add_argument("--roofline-reps", type=int, default=5)
     ap.add_argument("--unfused", action="store_true", help="append as its own launch before each attention launch")
     args = ap.parse_args()
@@ -437,108 +690,21 @@ def main():
     if args.config == "formats":
         return bench_formats(args)
 
-    log(f"[bench] building {args.config} cache ...")
-    t0 = time.perf_counter()
-    stack = DecodeStack(cfg, dev)
-    torch.cuda.synchronize()
-    build_s = time.perf_counter() - t0
-    log(f"[bench] cache built in {build_s:.1f} s")
-
-    with_append = args.config != "single"
-    step_fn = (lambda: stack.step(with_append, fused=not args.unfused))
-    if args.no_graph:
-        for _ in range(args.warmup):
-            step_fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for _ in range(args.steps):
-            step_fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms, wall = e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
-        step_stats = None
-    else:
-        g = capture(step_fn)
-        log("[bench] graph captured; timing")
-        ms, wall = time_graph(g, args.steps, args.warmup)
-        step_stats = replay_stats(g, 20)
-    # attention-only step, and the step with the append as its own launch (context)
-    g_attn = capture(lambda: stack.step(False))
-    ms_attn, _ = time_graph(g_attn, args.steps, 2)
-    ms_unfused = None
-    if with_append and not args.unfused:
-        g_unf = capture(lambda: stack.step(True, fused=False))
-        ms_unfused, _ = time_graph(g_unf, args.steps, 2)
-        del g_unf
-    log(f"[bench] step {ms:.4f} ms (attention only {ms_attn:.4f} ms, append as its own launch {ms_unfused} ms)")
-
-    # the dominant kernel (decode attention): its average launch duration is the
-    # attention-only step (one launch per layer, replayed as a graph on the stream the kernels
-    # run on, timed with events over the whole timed region) divided by the layer count;
-    # event pairs around single eager launches are reported beside it (they add a few us of
-    # marker overhead per launch)
-    n_layers = len(cfg["pairs"])
-    dbytes = stack.decode_bytes()
-    launch_us = ms_attn * 1e3 / n_layers
-    achieved = sum(dbytes) / (ms_attn * 1e-3) / 1e9
-    durs = per_launch_durations(stack.decode_layer, n_layers, args.roofline_reps)
-    log(f"[bench] decode kernel avg {launch_us:.2f} us/launch (graph), "
-        f"{sum(durs) / n_layers * 1e3:.2f} us (eager, event pairs); {achieved:.1f} GB/s")
-
-    step_bytes = stack.alg_bytes(with_append)
-    tokens_per_s = stack.B * 1000.0 / ms
-    quality = quality_report(stack) if with_append else None
-    if quality:
-        for name, r in quality["layers"].items():
-            log(f"[bench] {name} (layer {r['layer']}): K rel RMS {r['k_rel_rms']:.4f}, V {r['v_rel_rms']:.4f}; "
-                f"attention vs fp32 max abs {r['attn_max_abs_vs_fp32']:.2e}, rel RMS {r['attn_rel_rms_vs_fp32']:.4f}")
-    cpu = None
-    if args.cpu_seqs > 0 and args.config != "single":
-        log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequences x {n_layers} layers ...")
-        t_cpu, attended = cpu_baseline_decode(cfg, stack, args.cpu_seqs)
-        cpu = {"value": args.cpu_seqs / t_cpu, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{args.cpu_seqs} of {stack.B} sequences ({attended // n_layers} attended tokens per "
-                         f"layer), all {n_layers} layers: append + binary64 attention (packing of the sample "
-                         f"not timed), single thread"}
-        log(f"[bench] CPU oracle {t_cpu:.1f} s -> {cpu['value']:.3f} tokens/s")
-
-    rec = {
-        "metric": "mixed-precision KV decode-attn tokens/s + packed-KV GB/s (% HBM peak), 1 GPU",
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": stack_dtype(stack),
-        "data": "synthetic (seeded Irwin-Hall N(0,1) K/V/q, 3 outlier key channels x10 per layer and head)",
-        "config": {"workload": cfg["workload"], "batch": stack.B, "context": stack.C,
-                   "attended_tokens": stack.L, "mean_attended_tokens": float(stack.attend.mean()), "layers": n_layers, "n_q_heads": stack.Hq,
-                   "n_kv_heads": stack.H, "head_dim": 128, "equiv_bits": kvq.kvq_equiv_bits(stack.model),
-                   "graph": not args.no_graph, "fused_append": with_append and not args.unfused,
-                   "keys": "per-token" if stack.k_mode else "per-channel"},
-        "packed_kv_gbps": step_bytes / (ms * 1e-3) / 1e9,
-        "packed_kv_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "step_alg_bytes": step_bytes,
-        "attention_only_ms_per_step": ms_attn,
-        "unfused_append_ms_per_step": ms_unfused,
-        "wall_s_timed": wall,
-        "step_ms_median_min": step_stats,
-        "cache_build_s": build_s,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
-                     "kernel": "decode_kernel (kvq_decode_attn)",
-                     "avg_launch_us": launch_us,
-                     "avg_launch_us_eager_events": sum(durs) / n_layers * 1e3,
-                     "alg_bytes_per_launch": sum(dbytes) / n_layers},
-        "cpu_baseline": cpu,
-        "quantization_error": quality,
-    }
+    headline = args.config == "llama"
+    rec = decode_workload(args.config, args, dev, flush_step=headline)
+    if headline and not args.headline_only:
+        # the other four workloads, each timed and roofline-measured like the headline, with
+        # its own CPU baseline leg: nested records of the same JSON line
+        others = {}
+        for name in ("single", "qwen", "ragged"):
+            sub = argparse.Namespace(**vars(args))
+            sub.steps, sub.warmup = min(args.steps, 20), min(args.warmup, 3)
+            sub.quality = False
+            others[name] = decode_workload(name, sub, dev)
+        sub = argparse.Namespace(**vars(args))
+        sub.steps, sub.warmup = min(args.steps, 20), min(args.warmup, 3)
+        others["pack"] = pack_workload(sub, dev)
+        rec["workloads"] = others
     print(json.dumps(rec), flush=True)
 
 
@@ -585,7 +751,7 @@ def bench_formats(args):
     print(json.dumps(rec), flush=True)
 
 
-def bench_pack(cfg, args):
+def bench_pack(cfg, args, emit=True):
     """Prefill pack of 32768 bf16 tokens per layer for all 32 layers; source GB/s."""
     import torch
     import synth
@@ -630,7 +796,43 @@ def bench_pack(cfg, args):
                      "avg_launch_us": launch_us, "alg_bytes_per_launch": (src_bytes + page_bytes) / len(caches)},
         "cpu_baseline": None,
     }
-    print(json.dumps(rec), flush=True)
+    del g, ks, vs, caches
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"[bench] pack: {ms:.4f} ms per 32-layer step, {rec['value']:.0f} GB/s of bf16 source, "
+        f"{launch_us:.2f} us per launch, frac {achieved / HBM_PEAK_GBPS:.3f}")
+    if getattr(args, "cpu_baseline", True):
+        rec["cpu_baseline"] = cpu_baseline_pack(cfg)
+        log(f"[bench] pack: CPU oracle {rec['cpu_baseline']['value']:.4g} GB/s of source")
+    if emit:
+        print(json.dumps(rec), flush=True)
+    return rec
+
+
+def cpu_baseline_pack(cfg, pages_per_layer=64):
+    """The oracle's quantize-on-write of the first `pages_per_layer` 32-token pages of every
+    layer (one core), extrapolated by pages to the whole prefill; bf16 source GB/s."""
+    import numpy as np
+    import oracle as orc
+    import synth
+    H, T = cfg["n_kv_heads"], cfg["context"]
+    n = pages_per_layer * 32
+    secs = 0.0
+    with OneCore():
+        for l, (kb, vb) in enumerate(cfg["pairs"]):
+            cm = synth.outlier_mult(cfg["seed"], l, H, cfg["n_outliers"])
+            k = _bits16(synth.fill(cfg["seed"], synth.KIND_K, l, 1, n, H, chan_mult=cm))
+            v = _bits16(synth.fill(cfg["seed"], synth.KIND_V, l, 1, n, H))
+            bt = np.arange(pages_per_layer, dtype=np.int32).reshape(1, pages_per_layer)
+            pages, rk, rv = orc.new_cache(kb, vb, H, 1, pages_per_layer)
+            t0 = time.perf_counter()
+            orc.pack(kb, vb, k, v, [n], bt, pages, rk, rv)
+            secs += time.perf_counter() - t0
+    est = secs * (T / n)
+    src_bytes = 2 * T * H * 128 * 2 * len(cfg["pairs"])
+    return cpu_record(src_bytes / est / 1e9, "GB/s (bf16 source)",
+                      f"the first {pages_per_layer} of {T // 32} pages of every layer; step time extrapolated by "
+                      f"pages ({est:.1f} s per 32-layer prefill)", extrapolated=True)
 
 
 def bench_sweep(args):

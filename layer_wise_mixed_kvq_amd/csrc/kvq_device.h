@@ -18,8 +18,8 @@ struct PageLayout {
     static constexpr int kKCodes = 0;                       // 32 rows x 16*KB bytes
     static constexpr int kKRowBytes = 16 * KB;
     static constexpr int kKSz = 512 * KB;                   // 128 x u32 (s16 | z16 << 16)
-    static constexpr int kVCodes = 512 * KB + 512;          // 128 rows x 4*VB bytes
-    static constexpr int kVRowBytes = 4 * VB;
+    static constexpr int kVCodes = 512 * KB + 512;          // 512*VB bytes in MFMA chunk order: lane l's
+                                                            // 8*VB bytes at 8*VB*l
     static constexpr int kVSz = 512 * (KB + VB) + 512;      // 32 tokens x 4 groups x u32
     static constexpr int kBytes = 512 * (KB + VB + 2);
 };

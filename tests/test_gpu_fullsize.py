@@ -2,12 +2,16 @@
 
 The device builds the whole cache exactly as the benchmark does and runs one full step
 (append + decode attention for every layer, library-chosen split plan).  The oracle then
-recomputes sampled (layer, sequence) pairs one at a time from the same seeded inputs,
-regenerated on the host:
+recomputes (layer, sequence) pairs one at a time from the same seeded inputs, regenerated on
+the host, in a thread pool (the oracle and the generator are C called through ctypes, which
+releases the interpreter lock):
   * packed pages (reached through the shared, possibly shuffled block table) and the live
     residual slots after the append: bit-exact;
   * out and lse of that sequence: within 2e-4 / 1e-4 (relative) of the binary64 oracle.
-The prefill pack workload is checked on sampled pages the same way.
+The Llama step is compared at every (layer, sequence) pair, the Qwen step at every layer for
+eight sequences; two more steps start one token short of a page boundary (contexts 4095 and
+8191), so that every sequence's append completes and quantizes a page inside the fused launch.
+The prefill pack workload is checked on sampled pages.
 """
 import numpy as np
 import pytest
@@ -53,31 +57,43 @@ def _oracle_sequence(orc, cfg, l, b, C):
     return pages, rk, rv, out, lse
 
 
+def _workers():
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def _check_samples(orc, stack, samples, what):
+    """Every (layer, sequence) pair of `samples`, the oracle's side computed in a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+    import synth
     import torch
     cfg = stack.cfg
-    for l, b in samples:
-        C = int(stack.lens[b])
-        log(f"{what}: layer {l} {cfg['pairs'][l]} sequence {b} ({C} + 1 tokens)")
-        pages_o, rk_o, rv_o, out_o, lse_o = _oracle_sequence(orc, cfg, l, b, C)
-        n_full = (C + 1) // 32
-        ids = torch.from_numpy(stack.block_table_host[b, :n_full].astype(np.int64)).to(stack.caches[l].pages.device)
-        dev_pages = stack.caches[l].pages.index_select(0, ids).cpu().numpy()
-        assert np.array_equal(dev_pages, pages_o[:n_full]), f"{what}: layer {l} seq {b}: packed pages differ"
-        n_live = (C + 1) % 32
-        rk_d = _bits(stack.caches[l].resid_k[b].cpu())
-        rv_d = _bits(stack.caches[l].resid_v[b].cpu())
-        assert np.array_equal(rk_d[:, :n_live], rk_o[0][:, :n_live]), f"{what}: layer {l} seq {b}: resid K"
-        assert np.array_equal(rv_d[:, :n_live], rv_o[0][:, :n_live]), f"{what}: layer {l} seq {b}: resid V"
-        out_d = stack.out[l][b:b + 1].cpu().numpy()
-        lse_d = stack.lse[l][b:b + 1].cpu().numpy()
-        assert_attention_close(out_d, lse_d, out_o, lse_o, f"{what}: layer {l} seq {b}")
+    synth.fill(0, synth.KIND_K, 0, 1, 1, 1)          # load the host generator before the threads start
+    log(f"{what}: {len(samples)} (layer, sequence) pairs, {_workers()} oracle threads")
+    with ThreadPoolExecutor(_workers()) as ex:
+        futs = [ex.submit(_oracle_sequence, orc, cfg, l, b, int(stack.lens[b])) for l, b in samples]
+        for (l, b), fut in zip(samples, futs):
+            C = int(stack.lens[b])
+            pages_o, rk_o, rv_o, out_o, lse_o = fut.result()
+            n_full = (C + 1) // 32
+            ids = torch.from_numpy(stack.block_table_host[b, :n_full].astype(np.int64)).to(stack.caches[l].pages.device)
+            dev_pages = stack.caches[l].pages.index_select(0, ids).cpu().numpy()
+            assert np.array_equal(dev_pages, pages_o[:n_full]), f"{what}: layer {l} seq {b}: packed pages differ"
+            n_live = (C + 1) % 32
+            rk_d = _bits(stack.caches[l].resid_k[b].cpu())
+            rv_d = _bits(stack.caches[l].resid_v[b].cpu())
+            assert np.array_equal(rk_d[:, :n_live], rk_o[0][:, :n_live]), f"{what}: layer {l} seq {b}: resid K"
+            assert np.array_equal(rv_d[:, :n_live], rv_o[0][:, :n_live]), f"{what}: layer {l} seq {b}: resid V"
+            out_d = stack.out[l][b:b + 1].cpu().numpy()
+            lse_d = stack.lse[l][b:b + 1].cpu().numpy()
+            assert_attention_close(out_d, lse_d, out_o, lse_o, f"{what}: layer {l} seq {b}")
+    log(f"{what}: all {len(samples)} pairs match")
 
 
-def _full_step(name):
+def _full_step(name, **override):
     import torch
     import bench
-    stack = bench.DecodeStack(bench.CONFIGS[name], torch.device("cuda:0"))
+    stack = bench.DecodeStack(dict(bench.CONFIGS[name], **override), torch.device("cuda:0"))
     stack.step(with_append=True)
     torch.cuda.synchronize()
     return stack
@@ -92,17 +108,40 @@ def _release():
 
 
 def test_llama_c325_full_size(kvq, orc):
-    """32 layers, 32/8 heads, batch 16, 4096 cached + 1 appended token, C3.25 table."""
+    """32 layers, 32/8 heads, batch 16, 4096 cached + 1 appended token, C3.25 table: every
+    (layer, sequence) pair."""
     stack = _full_step("llama")
-    _check_samples(orc, stack, [(0, 0), (5, 9), (28, 15), (31, 3), (16, 12)], "llama")
+    _check_samples(orc, stack, [(l, b) for l in range(32) for b in range(16)], "llama")
     del stack
     _release()
 
 
+def test_llama_c325_full_size_flushing_step(kvq, orc):
+    """As above with 4095 cached tokens: every sequence's appended token completes page 127,
+    which the fused launch quantizes and attends over; every (layer, sequence) pair."""
+    stack = _full_step("llama", context=4095)
+    _check_samples(orc, stack, [(l, b) for l in range(32) for b in range(16)], "llama flush")
+    del stack
+    _release()
+
+
+QWEN_SEQS = [0, 9, 18, 27, 36, 45, 54, 63]
+
+
 def test_qwen_c40_full_size(kvq, orc):
-    """28 layers, 28/4 heads (G = 7), batch 64, 8192 cached + 1 appended token, C4.0 table."""
+    """28 layers, 28/4 heads (G = 7), batch 64, 8192 cached + 1 appended token, C4.0 table:
+    every layer, eight sequences."""
     stack = _full_step("qwen")
-    _check_samples(orc, stack, [(0, 0), (6, 33), (12, 63), (27, 17)], "qwen")
+    _check_samples(orc, stack, [(l, b) for l in range(28) for b in QWEN_SEQS], "qwen")
+    del stack
+    _release()
+
+
+def test_qwen_c40_full_size_flushing_step(kvq, orc):
+    """8191 cached tokens: every append completes page 255 inside the fused launch; every
+    layer, four sequences."""
+    stack = _full_step("qwen", context=8191)
+    _check_samples(orc, stack, [(l, b) for l in range(28) for b in QWEN_SEQS[::2]], "qwen flush")
     del stack
     _release()
 
@@ -110,12 +149,12 @@ def test_qwen_c40_full_size(kvq, orc):
 def test_ragged_paged_full_size(kvq, orc):
     """Batch 256, lengths U{1024..32768}, physical pages a seeded permutation shared by all
     layers.  Samples: the shortest and the longest sequence, one whose append flushes a
-    page (length mod 32 == 31), one more."""
+    page (length mod 32 == 31), one more; every third layer."""
     stack = _full_step("ragged")
     lens = stack.lens
     flush = int(np.nonzero(lens % 32 == 31)[0][0]) if np.any(lens % 32 == 31) else 1
     seqs = [int(np.argmin(lens)), int(np.argmax(lens)), flush, 100]
-    samples = [(l, b) for l, b in zip([2, 17, 29, 10], seqs)] + [(30, flush)]
+    samples = [(l, b) for l in range(0, 32, 3) for b in seqs]
     _check_samples(orc, stack, samples, "ragged")
     del stack
     _release()

@@ -274,6 +274,32 @@ kvq_status kvq_append_decode_attn(const kvq_model *model, int32_t layer, const k
                                   int32_t pages_per_split, float *out, float *lse, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): kvq_append_decode_attn without a
+ * workspace argument.  The split partials and split counters live in a device array of the
+ * library (one per GPU, held until the process ends): KVQ_NOALLOC_MAX_COUNTERS counters at a
+ * fixed place, which every call leaves at zero, then at most KVQ_NOALLOC_MAX_PARTIAL_BYTES of
+ * partials.  The first call on a GPU zeroes that GPU's counters with a fill kernel on
+ * `stream`.  Nothing is allocated: no hipMalloc, hipFree or allocating library routine.
+ *   Arguments and results as for kvq_append_decode_attn.
+ *   Returns KVQ_ERR_WORKSPACE when batch * n_kv_heads exceeds KVQ_NOALLOC_MAX_COUNTERS or
+ *   the partials exceed KVQ_NOALLOC_MAX_PARTIAL_BYTES (kvq_noalloc_scratch_bytes gives their
+ *   size), before anything is launched.  The KVQ_DEBUG checks (which wait for the stream)
+ *   are not run.
+ *   All calls on one GPU share the array: calls that overlap in time on one GPU (on
+ *   different streams, or from different threads without ordering) race. */
+#define KVQ_NOALLOC_MAX_COUNTERS 65536
+#define KVQ_NOALLOC_MAX_PARTIAL_BYTES (32u << 20)
+kvq_status kvq_append_decode_attn_noalloc(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                                          const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,
+                                          kvq_dtype q_dtype, const void *q, int32_t max_seq_len,
+                                          int32_t pages_per_split, float *out, float *lse, void *stream);
+
+/* Partial bytes a kvq_append_decode_attn_noalloc call of this shape uses (compare with
+ * KVQ_NOALLOC_MAX_PARTIAL_BYTES); 0 for an invalid model or shape. */
+size_t kvq_noalloc_scratch_bytes(const kvq_model *model, int32_t batch, int32_t max_seq_len,
+                                 int32_t pages_per_split);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ from ._native import (KVQ_BF16, KVQ_F32, KVQ_LAYER_BF16, KVQ_LAYER_FP8, KVQ_LAYE
 HEAD_DIM = 128
 GROUP = 32
 
-__all__ = ["Model", "KEYS_PER_CHANNEL", "KEYS_PER_TOKEN", "LAYER_INT", "LAYER_FP8", "LAYER_BF16", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_dequant", "kvq_decode_attn", "kvq_append_decode_attn",
+__all__ = ["Model", "KEYS_PER_CHANNEL", "KEYS_PER_TOKEN", "LAYER_INT", "LAYER_FP8", "LAYER_BF16", "LayerCache", "KvqError", "kvq_pack", "kvq_append", "kvq_dequant", "kvq_decode_attn", "kvq_append_decode_attn", "kvq_append_decode_attn_noalloc", "kvq_noalloc_scratch_bytes",
            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_head_page_bytes",
            "kvq_page_bytes", "kvq_equiv_bits", "kvq_format_version", "lib"]
 
@@ -292,3 +292,39 @@ def kvq_append_decode_attn(model: Model, layer: int, cache: LayerCache, k_new, v
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
           "kvq_append_decode_attn")
     return out, lse
+
+
+def kvq_append_decode_attn_noalloc(model: Model, layer: int, cache: LayerCache, k_new, v_new, pos, q,
+                                   max_seq_len: int, out, lse, pages_per_split: int = 0, stream=None):
+    """kvq_append_decode_attn with the library's own per-GPU scratch instead of a workspace:
+    the C call allocates nothing (the caller passes out [batch][n_q_heads][128] fp32 and lse
+    [batch][n_q_heads] fp32, or lse=False).  Calls that overlap on one GPU race."""
+    import torch
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (pos, "pos"), (q, "q"), (out, "out")):
+        _dev(t, n)
+    shape = (cache.batch, model.n_kv_heads, HEAD_DIM)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new / v_new must be {shape}")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("k_new / v_new must be bfloat16")
+    if pos.dtype != torch.int32 or pos.numel() != cache.batch:
+        raise ValueError("pos must be int32 [batch]")
+    if tuple(q.shape) != (cache.batch, model.n_q_heads, HEAD_DIM):
+        raise ValueError(f"q must be [{cache.batch}][{model.n_q_heads}][128]")
+    if tuple(out.shape) != (cache.batch, model.n_q_heads, HEAD_DIM) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [batch][n_q_heads][128]")
+    if lse is not False:
+        _dev(lse, "lse")
+        if tuple(lse.shape) != (cache.batch, model.n_q_heads) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [batch][n_q_heads]")
+    cs = cache.c_struct()
+    check(lib().kvq_append_decode_attn_noalloc(ctypes.byref(model.c), layer, ctypes.byref(cs), k_new.data_ptr(),
+                                               v_new.data_ptr(), pos.data_ptr(), _dtype_code(q), q.data_ptr(),
+                                               max_seq_len, pages_per_split, out.data_ptr(),
+                                               lse.data_ptr() if lse is not False else None, _stream(stream)),
+          "kvq_append_decode_attn_noalloc")
+    return out, lse
+
+
+def kvq_noalloc_scratch_bytes(model: Model, batch: int, max_seq_len: int, pages_per_split: int = 0) -> int:
+    return int(lib().kvq_noalloc_scratch_bytes(ctypes.byref(model.c), batch, max_seq_len, pages_per_split))

@@ -25,7 +25,8 @@ KVQ_LAYER_INT, KVQ_LAYER_FP8, KVQ_LAYER_BF16 = 0, 1, 2
 
 EXPORTED = ("kvq_status_str", "kvq_format_version", "kvq_head_page_bytes", "kvq_page_bytes",
             "kvq_equiv_bits", "kvq_validate_model", "kvq_pack", "kvq_append", "kvq_dequant",
-            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_decode_attn", "kvq_append_decode_attn")
+            "kvq_decode_workspace_bytes", "kvq_workspace_init", "kvq_decode_attn", "kvq_append_decode_attn",
+            "kvq_append_decode_attn_noalloc", "kvq_noalloc_scratch_bytes")
 
 
 class KvqModel(ctypes.Structure):
@@ -86,6 +87,11 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn.restype = ctypes.c_int
         L.kvq_append_decode_attn.argtypes = [mp, i32, cp, vp, vp, vp, ctypes.c_int, vp, i32, i32, vp, vp, vp, sz, vp]
         L.kvq_append_decode_attn.restype = ctypes.c_int
+        if hasattr(L, "kvq_append_decode_attn_noalloc"):
+            L.kvq_append_decode_attn_noalloc.argtypes = [mp, i32, cp, vp, vp, vp, ctypes.c_int, vp, i32, i32, vp, vp, vp]
+            L.kvq_append_decode_attn_noalloc.restype = ctypes.c_int
+            L.kvq_noalloc_scratch_bytes.argtypes = [mp, i32, i32, i32]
+            L.kvq_noalloc_scratch_bytes.restype = sz
         if hasattr(L, "kvq_profile_set_phase_buffer"):
             L.kvq_profile_set_phase_buffer.argtypes = [vp, sz]
             L.kvq_profile_set_phase_buffer.restype = None

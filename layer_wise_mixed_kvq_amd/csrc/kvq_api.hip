@@ -2,6 +2,8 @@
 // and workspace sizing, then one kernel launch per call on the caller's stream.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kvq.h"
 #include "kvq_codec.h"
 #include "kvq_debug.h"
@@ -262,10 +264,16 @@ kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, void *str
 
 namespace {
 
-kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache, kvq_dtype q_dtype,
-                         const void *q, const int32_t *seq_len, const uint16_t *k_new, const uint16_t *v_new,
-                         const int32_t *pos, int32_t max_seq_len, int32_t pages_per_split, float *out, float *lse,
-                         void *workspace, size_t workspace_bytes, void *stream)
+// Where a decode call keeps its split partials and split counters.
+struct DecodeScratch {
+    float *part_o;
+    float *part_ml;
+    int *counters;
+};
+
+kvq_status decode_checks(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache, kvq_dtype q_dtype,
+                         const void *q, const float *out, const float *lse, int32_t max_seq_len,
+                         int32_t pages_per_split)
 {
     kvq_status s = check_layer(model, layer, cache);
     if (s != KVQ_OK) return s;
@@ -273,15 +281,16 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     if (q_dtype != KVQ_BF16 && q_dtype != KVQ_F32) return KVQ_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return KVQ_ERR_ALIGNMENT;
+    return KVQ_OK;
+}
+
+kvq_status decode_launch(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache, kvq_dtype q_dtype,
+                         const void *q, const int32_t *seq_len, const uint16_t *k_new, const uint16_t *v_new,
+                         const int32_t *pos, int32_t max_seq_len, int pps, int n_splits, float *out, float *lse,
+                         const DecodeScratch &w, bool debug_checks, void *stream)
+{
     const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
-    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, max_seq_len);
-    const int n_splits = n_splits_for(max_seq_len, pps);
-    if (n_splits > 65535) return KVQ_ERR_UNSUPPORTED;
-    const kvq::DecodeWorkspace ws = kvq::decode_workspace_layout(cache->batch, H, G, n_splits);
-    if (!workspace || workspace_bytes < ws.bytes) return KVQ_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return KVQ_ERR_ALIGNMENT;
     kvq::DecodeParams p;
-    char *w = static_cast<char *>(workspace);
     p.q = q;
     p.seq_len = seq_len;
     p.pos = pos;
@@ -294,9 +303,9 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     p.scales = scales_of(model, layer, cache);
     p.out = out;
     p.lse = lse;
-    p.part_o = reinterpret_cast<float *>(w + ws.part_o_off);
-    p.part_ml = reinterpret_cast<float *>(w + ws.part_ml_off);
-    p.counters = reinterpret_cast<int *>(w + ws.counters_off);
+    p.part_o = w.part_o;
+    p.part_ml = w.part_ml;
+    p.counters = w.counters;
     p.n_pages = cache->n_pages;
     p.H = H;
     p.G = G;
@@ -312,12 +321,67 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
         if (kvq::g_phase_buf && kvq::g_phase_bytes >= need) p.phase_ts = kvq::g_phase_buf;
     }
 #endif
-    if (kvq::debug_checks_enabled()) {
-        s = kvq::debug_check_decode(p, q_dtype == KVQ_F32, static_cast<hipStream_t>(stream));
+    if (debug_checks && kvq::debug_checks_enabled()) {
+        const kvq_status s = kvq::debug_check_decode(p, q_dtype == KVQ_F32, static_cast<hipStream_t>(stream));
         if (s != KVQ_OK) return s;
     }
     return hip_status(kvq::launch_decode(model->k_bits[layer], model->v_bits[layer], layer_code(model, layer), p,
                                          q_dtype == KVQ_F32, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache, kvq_dtype q_dtype,
+                         const void *q, const int32_t *seq_len, const uint16_t *k_new, const uint16_t *v_new,
+                         const int32_t *pos, int32_t max_seq_len, int32_t pages_per_split, float *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    kvq_status s = decode_checks(model, layer, cache, q_dtype, q, out, lse, max_seq_len, pages_per_split);
+    if (s != KVQ_OK) return s;
+    const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
+    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, max_seq_len);
+    const int n_splits = n_splits_for(max_seq_len, pps);
+    if (n_splits > 65535) return KVQ_ERR_UNSUPPORTED;
+    const kvq::DecodeWorkspace ws = kvq::decode_workspace_layout(cache->batch, H, G, n_splits);
+    if (!workspace || workspace_bytes < ws.bytes) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGNMENT;
+    char *w = static_cast<char *>(workspace);
+    const DecodeScratch sc = {reinterpret_cast<float *>(w + ws.part_o_off), reinterpret_cast<float *>(w + ws.part_ml_off),
+                              reinterpret_cast<int *>(w + ws.counters_off)};
+    return decode_launch(model, layer, cache, q_dtype, q, seq_len, k_new, v_new, pos, max_seq_len, pps, n_splits, out,
+                         lse, sc, true, stream);
+}
+
+// ---- the library's own decode scratch, for kvq_append_decode_attn_noalloc --------------
+// One file-scope device array per GPU: split counters at a fixed offset (so every call finds
+// them at zero, whatever its shape), then the split partials.  Host code uses the device
+// address hipGetSymbolAddress returns for the current device, never the array's name.
+constexpr size_t kScratchCounterBytes = static_cast<size_t>(KVQ_NOALLOC_MAX_COUNTERS) * sizeof(int);
+constexpr size_t kScratchBytes = kScratchCounterBytes + KVQ_NOALLOC_MAX_PARTIAL_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+static ScratchSlot g_scratch[kMaxDevices];
+
+// The scratch's device address on the current device; the first call on a device also zeroes
+// its counters (a fill kernel on `stream`).
+static kvq_status scratch_for_current_device(void **ptr, hipStream_t stream)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_HIP;
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&] {
+        void *p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess) slot.err = kvq::launch_zero_fill(p, kScratchCounterBytes, stream);
+        if (slot.err == hipSuccess) slot.ptr = p;
+    });
+    if (slot.err != hipSuccess || !slot.ptr) return KVQ_ERR_HIP;
+    *ptr = slot.ptr;
+    return KVQ_OK;
 }
 
 }  // namespace
@@ -341,6 +405,42 @@ kvq_status kvq_append_decode_attn(const kvq_model *model, int32_t layer, const k
     if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
     return decode_common(model, layer, cache, q_dtype, q, nullptr, k_new, v_new, pos, max_seq_len,
                          pages_per_split, out, lse, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_append_decode_attn_noalloc(const kvq_model *model, int32_t layer, const kvq_layer_cache *cache,
+                                          const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,
+                                          kvq_dtype q_dtype, const void *q, int32_t max_seq_len,
+                                          int32_t pages_per_split, float *out, float *lse, void *stream)
+{
+    if (!k_new || !v_new || !pos) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
+    kvq_status s = decode_checks(model, layer, cache, q_dtype, q, out, lse, max_seq_len, pages_per_split);
+    if (s != KVQ_OK) return s;
+    const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
+    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, max_seq_len);
+    const int n_splits = n_splits_for(max_seq_len, pps);
+    if (n_splits > 65535) return KVQ_ERR_UNSUPPORTED;
+    const kvq::DecodeWorkspace ws = kvq::decode_workspace_layout(cache->batch, H, G, n_splits);
+    // the partials take everything before the workspace layout's counters
+    if (static_cast<long long>(cache->batch) * H > KVQ_NOALLOC_MAX_COUNTERS ||
+        ws.counters_off > static_cast<size_t>(KVQ_NOALLOC_MAX_PARTIAL_BYTES))
+        return KVQ_ERR_WORKSPACE;
+    void *base = nullptr;
+    s = scratch_for_current_device(&base, static_cast<hipStream_t>(stream));
+    if (s != KVQ_OK) return s;
+    char *part = static_cast<char *>(base) + kScratchCounterBytes;
+    const DecodeScratch sc = {reinterpret_cast<float *>(part + ws.part_o_off),
+                              reinterpret_cast<float *>(part + ws.part_ml_off), static_cast<int *>(base)};
+    return decode_launch(model, layer, cache, q_dtype, q, nullptr, k_new, v_new, pos, max_seq_len, pps, n_splits,
+                         out, lse, sc, false, stream);
+}
+
+size_t kvq_noalloc_scratch_bytes(const kvq_model *model, int32_t batch, int32_t max_seq_len, int32_t pages_per_split)
+{
+    if (check_model(model) != KVQ_OK || batch <= 0 || max_seq_len < 0 || pages_per_split < 0) return 0;
+    const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
+    const int pps = plan_pages_per_split(pages_per_split, batch, H, max_seq_len);
+    return kvq::decode_workspace_layout(batch, H, G, n_splits_for(max_seq_len, pps)).counters_off;
 }
 
 }  // extern "C"

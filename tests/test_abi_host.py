@@ -162,6 +162,20 @@ def test_entry_points_reject_before_launch(kvq):
                              A, need, None) == N.KVQ_ERR_UNSUPPORTED
     assert L.kvq_workspace_init(None, 16, None) == N.KVQ_ERR_INVALID_ARG
     assert L.kvq_workspace_init(A + 4, 16, None) == N.KVQ_ERR_ALIGNMENT
+    # the scratch-backed fused entry point: argument errors, and shapes beyond its fixed
+    # maximum (more than KVQ_NOALLOC_MAX_COUNTERS (sequence, KV head) pairs, or more than
+    # KVQ_NOALLOC_MAX_PARTIAL_BYTES of partials), all before any HIP call
+    na = L.kvq_append_decode_attn_noalloc
+    assert na(mp, 0, ctypes.byref(good), None, A, A, N.KVQ_BF16, A, 64, 0, A, A, None) == N.KVQ_ERR_INVALID_ARG
+    assert na(mp, 0, ctypes.byref(good), A + 2, A, A, N.KVQ_BF16, A, 64, 0, A, A, None) == N.KVQ_ERR_ALIGNMENT
+    assert na(mp, 0, ctypes.byref(good), A, A, A, N.KVQ_BF16, A, 64, 0, None, A, None) == N.KVQ_ERR_INVALID_ARG
+    assert na(mp, 0, ctypes.byref(good), A, A, A, 3, A, 64, 0, A, A, None) == N.KVQ_ERR_UNSUPPORTED
+    wide = _fake_cache(kvq, batch=65535)           # 65535 * 2 KV heads > 65536 counters
+    assert na(mp, 0, ctypes.byref(wide), A, A, A, N.KVQ_BF16, A, 64, 0, A, A, None) == N.KVQ_ERR_WORKSPACE
+    long_ = _fake_cache(kvq, batch=64)            # 64 * 2 heads * 2**20 tokens: partials far beyond 32 MiB
+    assert na(mp, 0, ctypes.byref(long_), A, A, A, N.KVQ_BF16, A, 1 << 20, 1, A, A, None) == N.KVQ_ERR_WORKSPACE
+    assert L.kvq_noalloc_scratch_bytes(mp, 64, 1 << 20, 1) > (32 << 20)
+    assert 0 < L.kvq_noalloc_scratch_bytes(mp, 2, 64, 0) <= (32 << 20)
 
 
 def test_workspace_grows_with_splits(kvq):

@@ -105,13 +105,13 @@ int n_splits_for(int max_seq_len, int pps)
     return n > 0 ? n : 1;
 }
 
-// pages per split-K work item: the caller's value (at most 256: a workgroup's four waves
-// hold at most 64 page ids each), or the library's choice for 0
-int plan_pages_per_split(int requested, int batch, int H, int max_seq_len)
+// pages per split-K work item: the caller's value (at most 256: a workgroup's waves hold
+// at most 64 page ids each), or the library's choice for 0
+int plan_pages_per_split(int requested, int batch, int H, int G, int max_seq_len)
 {
     if (requested > 256) return 256;
     if (requested > 0) return requested;
-    return kvq::decode_default_pages_per_split(batch, H, max_seq_len / KVQ_GROUP);
+    return kvq::decode_default_pages_per_split(batch, H, G, max_seq_len / KVQ_GROUP);
 }
 
 }  // namespace
@@ -251,7 +251,7 @@ size_t kvq_decode_workspace_bytes(const kvq_model *model, int32_t batch, int32_t
 {
     if (check_model(model) != KVQ_OK || batch <= 0 || max_seq_len < 0 || pages_per_split < 0) return 0;
     const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
-    const int pps = plan_pages_per_split(pages_per_split, batch, H, max_seq_len);
+    const int pps = plan_pages_per_split(pages_per_split, batch, H, G, max_seq_len);
     return kvq::decode_workspace_layout(batch, H, G, n_splits_for(max_seq_len, pps)).bytes;
 }
 
@@ -314,10 +314,11 @@ kvq_status decode_launch(const kvq_model *model, int32_t layer, const kvq_layer_
     p.max_seq_len = max_seq_len;
     p.pages_per_split = pps;
     p.n_splits = n_splits;
+    p.waves = kvq::decode_waves_for(cache->batch, H, G);
     p.phase_ts = nullptr;
 #if defined(KVQ_PHASE_TIMERS)
     {
-        const size_t need = static_cast<size_t>(H) * cache->batch * n_splits * 4 * kvq::kPhaseStamps * 8;
+        const size_t need = static_cast<size_t>(H) * cache->batch * n_splits * 8 * kvq::kPhaseStamps * 8;
         if (kvq::g_phase_buf && kvq::g_phase_bytes >= need) p.phase_ts = kvq::g_phase_buf;
     }
 #endif
@@ -337,7 +338,7 @@ kvq_status decode_common(const kvq_model *model, int32_t layer, const kvq_layer_
     kvq_status s = decode_checks(model, layer, cache, q_dtype, q, out, lse, max_seq_len, pages_per_split);
     if (s != KVQ_OK) return s;
     const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
-    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, max_seq_len);
+    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, G, max_seq_len);
     const int n_splits = n_splits_for(max_seq_len, pps);
     if (n_splits > 65535) return KVQ_ERR_UNSUPPORTED;
     const kvq::DecodeWorkspace ws = kvq::decode_workspace_layout(cache->batch, H, G, n_splits);
@@ -417,7 +418,7 @@ kvq_status kvq_append_decode_attn_noalloc(const kvq_model *model, int32_t layer,
     kvq_status s = decode_checks(model, layer, cache, q_dtype, q, out, lse, max_seq_len, pages_per_split);
     if (s != KVQ_OK) return s;
     const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
-    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, max_seq_len);
+    const int pps = plan_pages_per_split(pages_per_split, cache->batch, H, G, max_seq_len);
     const int n_splits = n_splits_for(max_seq_len, pps);
     if (n_splits > 65535) return KVQ_ERR_UNSUPPORTED;
     const kvq::DecodeWorkspace ws = kvq::decode_workspace_layout(cache->batch, H, G, n_splits);
@@ -439,7 +440,7 @@ size_t kvq_noalloc_scratch_bytes(const kvq_model *model, int32_t batch, int32_t 
 {
     if (check_model(model) != KVQ_OK || batch <= 0 || max_seq_len < 0 || pages_per_split < 0) return 0;
     const int H = model->n_kv_heads, G = model->n_q_heads / model->n_kv_heads;
-    const int pps = plan_pages_per_split(pages_per_split, batch, H, max_seq_len);
+    const int pps = plan_pages_per_split(pages_per_split, batch, H, G, max_seq_len);
     return kvq::decode_workspace_layout(batch, H, G, n_splits_for(max_seq_len, pps)).counters_off;
 }
 

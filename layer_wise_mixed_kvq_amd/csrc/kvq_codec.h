@@ -138,11 +138,13 @@ __device__ __forceinline__ void encode_group(const float (&v)[kGroup], T *x, int
     // scale gives code 0.  For the finite scales of an fp16 word q comes from the
     // reciprocal: y = RN(1/s) is the hardware reciprocal (within 1 ulp) after one Newton
     // step (this holds for every significand that is not all ones, so for every fp16
-    // value -- checked exhaustively), q0 = RN(d y), and two corrections
-    // q <- q + (d - s q) y with exact residuals make it RN(d / s) (Markstein's theorem for
-    // the second; the first only has to make q faithful): five operations instead of the
-    // eleven of the general division, which remains for non-finite s or z (outside the
-    // input domain).  With s = 0, y = 0 makes every q 0.
+    // value), q0 = RN(d y), and two corrections q <- q + (d - s q) y with exact residuals
+    // make it RN(d / s) (Markstein's theorem for the second; the first only has to make q
+    // faithful): five operations instead of the eleven of the general division, which
+    // remains for non-finite s or z (outside the input domain).  With s = 0, y = 0 makes
+    // every q 0.  tests/test_gpu_codec_scales.py packs groups at every finite fp16 scale,
+    // with quotients at each half-integer and two ulps either side, at 2, 4 and 8 bits, and
+    // matches the oracle's correctly rounded division byte for byte.
     float q[kGroup];
     if (__builtin_isfinite(s) && __builtin_isfinite(z)) {
         const float y0 = __builtin_amdgcn_rcpf(s);
@@ -184,9 +186,10 @@ __device__ __forceinline__ int ktok_slot_channel(int a, int slot)
     return 32 * (k / 4) + 8 * a + 2 * (k % 4) + hh;
 }
 
-// Quantize the staged tiles of one page-head into `dst` (global).  All 256 threads of the
-// workgroup call it; with DEQUANT the tiles hold the dequantized values afterwards (valid
-// after the workgroup's next barrier).  KTOK selects the per-token key mode.
+// Quantize the staged tiles of one page-head into `dst` (global).  Every thread of the
+// workgroup calls it (at least 256: threads 256 and up only take part in the barriers);
+// with DEQUANT the tiles hold the dequantized values afterwards (valid after the
+// workgroup's next barrier).  KTOK selects the per-token key mode.
 template <int KB, int VB, bool DEQUANT = false, bool KTOK = false, typename T>
 __device__ void quantize_page(QuantSmemT<T> &sm, uint8_t *__restrict__ dst)
 {
@@ -197,10 +200,12 @@ __device__ void quantize_page(QuantSmemT<T> &sm, uint8_t *__restrict__ dst)
     // the thread's group: threads 0..127 a key group (channel tid, or in the per-token mode
     // token tid % 32 and channels 32 (tid / 32) ..), threads 128..255 the value group of
     // token (tid - 128) % 32 and channels 32 ((tid - 128) / 32) ..
+    const bool act = tid < kCodecThreads;
     const bool is_k = tid < kHeadDim;
     const int t = tid & (kGroup - 1), j = (tid & (kHeadDim - 1)) >> 5;
     float v[kGroup];
-    if (is_k) {
+    if (!act) {
+    } else if (is_k) {
         if constexpr (KTOK)
             load_group(&sm.k[t * kTileStride + kGroup * j], 1, v);
         else
@@ -210,7 +215,8 @@ __device__ void quantize_page(QuantSmemT<T> &sm, uint8_t *__restrict__ dst)
     }
     if constexpr (QuantSmemT<T>::kCodesOverTiles) __syncthreads();   // the codes overwrite the tiles
     uint32_t w;
-    if (is_k) {
+    if (!act) {
+    } else if (is_k) {
         if constexpr (KTOK) {
             encode_group<KB, DEQUANT>(v, &sm.k[t * kTileStride + kGroup * j], 1, w, &sm.kcode[t * kHeadDim + kGroup * j], 1);
             dst32[P::kKSz / 4 + kValueGroups * t + j] = w;
@@ -227,7 +233,7 @@ __device__ void quantize_page(QuantSmemT<T> &sm, uint8_t *__restrict__ dst)
     // K codes: dword d of the section holds 32/KB slots of one token row (consecutive
     // channels, or in the per-token mode the channels of ktok_slot_channel)
     constexpr int kPerWord = 32 / KB;
-    for (int d = tid; d < 128 * KB; d += kCodecThreads) {
+    for (int d = tid; act && d < 128 * KB; d += kCodecThreads) {
         const int t = d / (4 * KB), dr = d % (4 * KB);
         uint32_t w = 0;
 #pragma unroll
@@ -245,7 +251,7 @@ __device__ void quantize_page(QuantSmemT<T> &sm, uint8_t *__restrict__ dst)
     // r, r+16, ..., r+112.  Word dw of a chunk holds, in each 16-bit half hh, the codes of
     // k = dw*n .. dw*n + n-1 (n = 16/VB), k = 4*(c/16) + (t%4), token t = 8q + (t%4) + 4hh.
     constexpr int n = 16 / VB;
-    for (int d = tid; d < 128 * VB; d += kCodecThreads) {
+    for (int d = tid; act && d < 128 * VB; d += kCodecThreads) {
         const int u = d / (2 * VB), dw = d % (2 * VB);
         const int q = u >> 4, r = u & 15;
         uint32_t w = 0;
@@ -320,8 +326,8 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
     return (b & 0x80u) ? -v : v;
 }
 
-// Convert the staged tiles of one page-head into `dst` (global) in format FMT.  All 256
-// threads call it; every output dword is built from tile elements no other thread reads,
+// Convert the staged tiles of one page-head into `dst` (global) in format FMT.  Every thread
+// calls it (threads 256 and up do nothing); every output dword is built from tile elements no other thread reads,
 // so with DEQUANT the tiles are overwritten in place with the values the page stores
 // (E4M3 value * scale, binary32), valid after the workgroup's next barrier.
 template <int FMT, bool DEQUANT = false, typename T>
@@ -337,7 +343,7 @@ __device__ void quantize_page_float(QuantSmemT<T> &sm, uint8_t *__restrict__ dst
     uint32_t *v32 = reinterpret_cast<uint32_t *>(dst + FL::kV);
     constexpr int kPer = 4 / FL::kElem;                                // elements per dword
     constexpr int kWords = kGroup * kHeadDim / kPer;
-    for (int d = tid; d < kWords; d += kCodecThreads) {
+    for (int d = tid; tid < kCodecThreads && d < kWords; d += kCodecThreads) {
         // K: token-major
         {
             const int t = d / (kHeadDim / kPer), c0 = (d % (kHeadDim / kPer)) * kPer;

@@ -64,8 +64,12 @@
 namespace kvq {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup (NW): eight, one workgroup filling a CU, so that the CU's waves all
+// work on one split of one (sequence, KV head) and run out of pages together, when every
+// workgroup of the launch is resident at once (at most one per CU) and two waves per SIMD
+// fit (G <= 8); four otherwise, two workgroups per CU, so that one's merge and combine
+// overlap the other's pages.  decode_waves_for() is the host's choice.
+constexpr int kMaxWaves = 8;
 [[maybe_unused]] constexpr int kMaxGS = 4;                   // head slots per lane group: G <= 16
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kScoreScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e)/sqrt(128)
@@ -136,6 +140,39 @@ __device__ __forceinline__ void split3_bf16(float x0, float x1, uint32_t &hi, ui
     hi = bf16_pair(x0, x1, r0, r1);
     mid = bf16_pair(r0, r1, e0, e1);
     lo = bf16_pair(e0, e1, r0, r1);
+}
+
+// hi / lo split of two products a0 * s0, a1 * s1 with s0, s1 the fp16 in the low halves of
+// w0, w1: each product is formed from the fp16 operand directly by a mixed-precision
+// multiply-add (no conversion of s, no separate product), and lo from the very bits stored
+// as hi, as in split_hi / split_lo.
+__device__ __forceinline__ _Float16 lo_half(uint32_t w) { return __builtin_bit_cast(half2_t, w)[0]; }
+__device__ __forceinline__ _Float16 hi_half(uint32_t w) { return __builtin_bit_cast(half2_t, w)[1]; }
+
+__device__ __forceinline__ uint32_t fold_hi(float a0, float a1, uint32_t w0, uint32_t w1)
+{
+    const _Float16 x0 = static_cast<_Float16>(__builtin_fmaf(a0, static_cast<float>(lo_half(w0)), 0.0f));
+    const _Float16 x1 = static_cast<_Float16>(__builtin_fmaf(a1, static_cast<float>(lo_half(w1)), 0.0f));
+    uint32_t h = __builtin_bit_cast(uint32_t, half2_t{x0, x1});
+    __asm__ volatile("" : "+v"(h));
+    return h;
+}
+
+__device__ __forceinline__ uint32_t fold_lo(float a0, float a1, uint32_t w0, uint32_t w1, uint32_t hi)
+{
+    const float r0 = __builtin_fmaf(a0, static_cast<float>(lo_half(w0)), -static_cast<float>(lo_half(hi)));
+    const float r1 = __builtin_fmaf(a1, static_cast<float>(lo_half(w1)), -static_cast<float>(hi_half(hi)));
+    return __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(r0), static_cast<_Float16>(r1)});
+}
+
+// fp16 bits of 2^k, clamped to [smallest subnormal, infinity]: a threshold for fp16 scale
+// words (non-negative, so they order as unsigned integers)
+__device__ __forceinline__ uint32_t fp16_pow2_bits(int k)
+{
+    if (k > 15) return 0x7C00u;
+    if (k >= -14) return static_cast<uint32_t>(k + 15) << 10;
+    if (k >= -24) return 1u << (k + 24);
+    return 1u;
 }
 
 // LDS ordering inside one wave: the LDS executes one wave's DS instructions in issue
@@ -359,16 +396,17 @@ struct WaveLds {
     // (p s) parts, one block per value group: [part][head, + zero row][pair]
     static constexpr int kPPBlock = NP * (4 * GS + 1) * 20;
     alignas(16) uint32_t pp[PG][kPPBlock];
-    float p[4 * GS][48];                             // FP8 / BF16 layers: the page's softmax weights, [head][token]
+    alignas(16) float p[4 * GS][48];                 // FP8 / BF16 layers: the page's softmax weights, [head][token];
+                                                     // before the page loop: the residual tokens' weights
     float bv[4][4 * GS];                             // value zero terms at the end: [group][head]
     __device__ uint32_t *pp_row(int g, int part, int row) { return &pp[g][(part * (4 * GS + 1) + row) * 20]; }
 };
 
-template <int GS>
+template <int GS, int NW>
 struct MergeLds {
-    float o[kWaves][4 * GS][kHeadDim + 16];   // head rows 16 mod 64 words apart: the lane groups' writes miss each other's banks
-    float m[kWaves][4 * GS];
-    float l[kWaves][4 * GS];
+    float o[NW][4 * GS][kHeadDim + 16];   // head rows 16 mod 64 words apart: the lane groups' writes miss each other's banks
+    float m[NW][4 * GS];
+    float l[NW][4 * GS];
 };
 
 template <int GS>
@@ -379,22 +417,23 @@ struct ResidualLds {              // staging of the residual tokens (page-codec 
 
 template <int GS>
 struct ResidualOut {              // (m, l, o) of the residual tokens, kept for the merge
-    float o[4 * GS][kHeadDim];
+    alignas(16) float o[4 * GS][kHeadDim];
     float m[4 * GS];
     float l[4 * GS];
 };
 
-template <int GS, int KM>
+template <int GS, int KM, int NW>
 struct DecodeSmem {
-    float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128), for the residual tokens
+    alignas(16) float qs[4 * GS][kHeadDim];   // q * log2(e)/sqrt(128), for the residual tokens
     ResidualOut<GS> ro;
     union {
-        WaveLds<GS, KM> w[kWaves];
-        MergeLds<GS> merge;
+        WaveLds<GS, KM> w[NW];
+        MergeLds<GS, NW> merge;
         ResidualLds<GS> res;
     } u;
     int last;
     int early;
+    int bad;                      // some wave saw a page id outside the pool
 };
 
 #if defined(KVQ_PHASE_TIMERS)
@@ -404,7 +443,7 @@ __device__ __forceinline__ void phase_stamp(const DecodeParams &p, int k)
 {
     if (p.phase_ts && (threadIdx.x & 63) == 0) {
         const long long wg = blockIdx.x + static_cast<long long>(gridDim.x) * (blockIdx.y + static_cast<long long>(gridDim.y) * blockIdx.z);
-        unsigned long long *r = p.phase_ts + (wg * kWaves + (threadIdx.x >> 6)) * kPhaseStamps;
+        unsigned long long *r = p.phase_ts + (wg * kMaxWaves + (threadIdx.x >> 6)) * kPhaseStamps;
         r[k] = __builtin_amdgcn_s_memrealtime();
         if (k == 0) {
             // HW_REG_HW_ID (id 4) and HW_REG_XCC_ID (id 20), all 32 bits
@@ -453,55 +492,199 @@ __device__ __forceinline__ void wait_stores()
 }
 
 // ------------------------------------------------------------------------------------
-// residual tokens (at most 31, bf16), plain VALU, into LDS: (m, l, o) per head
+// residual tokens (bf16): (m, l, o) per head into LDS
 // ------------------------------------------------------------------------------------
-// The residual rows are requested at kernel start (16-byte chunks i = tid, tid + 256 of
-// the 32 x 128 bf16 tile, rows below nres only) and attended after the pages, so their
-// load latency is hidden behind the page work.
-// With the fused append the last row (nres - 1) is the new token, read from k_new / v_new.
-__device__ __forceinline__ void load_residual(const DecodeParams &p, long long bh, int nres, bool append,
-                                              uint4 (&kv)[4])
+// With a flush split 0's workgroup attends them after its page loop.  The whole 32 x 128
+// tile is requested right after the first page, in 16-byte chunks, chunk i = tid, tid + NT,
+// ... (token i / 16, channels 8 (i % 16) .. +7), and with the fused append the chunk of the
+// new token at the same channels.
+template <int NT>
+__device__ __forceinline__ void load_residual(const DecodeParams &p, long long bh, bool append,
+                                              uint4 (&kv)[4 * (512 / NT)])
 {
+    constexpr int KC = 512 / NT;
     const uint4 *rk = reinterpret_cast<const uint4 *>(p.resid_k + bh * kGroup * kHeadDim);
     const uint4 *rv = reinterpret_cast<const uint4 *>(p.resid_v + bh * kGroup * kHeadDim);
-    const uint4 *nk = reinterpret_cast<const uint4 *>(p.k_new + bh * kHeadDim);
-    const uint4 *nv = reinterpret_cast<const uint4 *>(p.v_new + bh * kHeadDim);
+    const uint4 *nk = reinterpret_cast<const uint4 *>((append ? p.k_new : p.resid_k) + bh * kHeadDim);
+    const uint4 *nv = reinterpret_cast<const uint4 *>((append ? p.v_new : p.resid_v) + bh * kHeadDim);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int i = threadIdx.x + k * kThreads, row = i / (kHeadDim / 8), col = i % (kHeadDim / 8);
-        const bool live = row < nres;
-        const bool fresh = append && row == nres - 1;
-        kv[k] = !live ? make_uint4(0u, 0u, 0u, 0u) : fresh ? nk[col] : rk[i];
-        kv[2 + k] = !live ? make_uint4(0u, 0u, 0u, 0u) : fresh ? nv[col] : rv[i];
+    for (int k = 0; k < KC; ++k) {
+        const int i = threadIdx.x + k * NT, col = i % (kHeadDim / 8);
+        kv[k] = rk[i];
+        kv[KC + k] = rv[i];
+        kv[2 * KC + k] = nk[col];
+        kv[3 * KC + k] = nv[col];
     }
 }
 
-// Fused append: the new token (row nres - 1) is also stored into its residual slot; when it
-// completes a group (flush) the 32 rows are quantized into their page `flush_page` (same
-// codec and bytes as kvq_append) and the tile is replaced by its dequantized values, which
-// are then attended.  Returns false if the flush page id is outside the pool.
-template <int KB, int VB, int GS, int KM>
-__device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS, KM> &sm, const uint4 (&kv)[4], int nres, int G,
-                                long long bh, bool append, bool flush, int flush_page)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Without a flush (at most 31 tokens) wave 0 of split 0 attends the residual tokens before
+// its page loop, from registers, with no barrier.  Lane roles:
+//   keys:   token t = lane % 32, channels 64 (lane / 32) .. +63 (eight 16-byte loads)
+//   values: channels 2 lane, 2 lane + 1 of every token (one 4-byte load per token)
+// Rows past nres - 1 reload row nres - 1 (the same addresses: cache hits) and are masked.
+// With the fused append the last row (nres - 1) is the new token, read from k_new / v_new.
+struct ResidualWaveRegs {
+    uint4 k[8];
+    uint32_t v[kGroup];
+};
+
+__device__ __forceinline__ void load_residual_wave(const DecodeParams &p, long long bh, int nres, bool append,
+                                                   ResidualWaveRegs &r)
 {
-    ResidualLds<GS> &R = sm.u.res;
-    const int tid = threadIdx.x;
-    KVQ_STAMP(12);
+    const int lane = threadIdx.x & 63;
+    const int t = min(lane & 31, nres - 1), half = lane >> 5;
+    const uint16_t *krow = append && t == nres - 1 ? p.k_new + bh * kHeadDim
+                                                   : p.resid_k + (bh * kGroup + t) * kHeadDim;
+    const uint4 *k4 = reinterpret_cast<const uint4 *>(krow + 64 * half);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int i = tid + k * kThreads, row = i / (kHeadDim / 8), col = 8 * (i % (kHeadDim / 8));
+    for (int i = 0; i < 8; ++i) r.k[i] = k4[i];
+#pragma unroll
+    for (int tt = 0; tt < kGroup; ++tt) {
+        const int row = min(tt, nres - 1);
+        const uint16_t *vrow = append && row == nres - 1 ? p.v_new + bh * kHeadDim
+                                                         : p.resid_v + (bh * kGroup + row) * kHeadDim;
+        r.v[tt] = reinterpret_cast<const uint32_t *>(vrow)[lane];
+    }
+}
+
+// The wave's residual attention into sm.ro: scores against q~ (sm.qs, which this wave
+// wrote), softmax over the nres tokens, values weighted through the wave's own WaveLds::p;
+// the fused append also stores the new token into its residual slot.
+template <int GS, int KM, int NW>
+__device__ void residual_wave(const DecodeParams &p, DecodeSmem<GS, KM, NW> &sm, WaveLds<GS, KM> &W,
+                              const ResidualWaveRegs &r, int nres, int G, long long bh, bool append)
+{
+    constexpr int HS = 4 * GS;
+    const int lane = threadIdx.x & 63, t = lane & 31, half = lane >> 5;
+    KVQ_STAMP(12);
+    if (append) {
+        const long long row = (bh * kGroup + (nres - 1)) * kHeadDim;
+        if (t == nres - 1) {
+            uint4 *dk = reinterpret_cast<uint4 *>(p.resid_k + row + 64 * half);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dk[i] = r.k[i];
+        }
+#pragma unroll
+        for (int tt = 0; tt < kGroup; ++tt)
+            if (tt == nres - 1) reinterpret_cast<uint32_t *>(p.resid_v + row)[lane] = r.v[tt];
+    }
+    const bool live = t < nres;
+    // scores of every head (independent chains): each 8-channel chunk of the key row is
+    // widened once and used by every head, then the softmax of each head
+    float sc[HS];
+#pragma unroll
+    for (int h = 0; h < HS; ++h) sc[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 kw = r.k[i];
+        const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
+                             bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+#pragma unroll
+        for (int h = 0; h < HS; ++h) {
+            if (h >= G) break;
+            const float4 *qrow = reinterpret_cast<const float4 *>(&sm.qs[h][64 * half + 8 * i]);
+            const float4 qa = qrow[0], qb = qrow[1];
+            float acc = sc[h];
+            acc = fmaf(qa.x, kf[0], acc);
+            acc = fmaf(qa.y, kf[1], acc);
+            acc = fmaf(qa.z, kf[2], acc);
+            acc = fmaf(qa.w, kf[3], acc);
+            acc = fmaf(qb.x, kf[4], acc);
+            acc = fmaf(qb.y, kf[5], acc);
+            acc = fmaf(qb.z, kf[6], acc);
+            acc = fmaf(qb.w, kf[7], acc);
+            sc[h] = acc;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < HS; ++h) {
+        if (h >= G) continue;
+        const float acc = sc[h] + __shfl_xor(sc[h], 32);
+        const float x = live ? acc : -INFINITY;
+        // tokens 0-15 are lane group 0, tokens 16-31 lane group 1 (groups 2, 3 repeat them)
+        const float mr = row_max(x);
+        const float m = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 0)),
+                              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 16)));
+        const float e = live ? __builtin_amdgcn_exp2f(x - m) : 0.0f;
+        const float er = row_sum(e);
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(er), 0)) +
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(er), 16));
+        if (half == 0) W.p[h][t] = e;
+        if (lane == 0) {
+            sm.ro.m[h] = m;
+            sm.ro.l[h] = l;
+        }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int h = 0; h < HS; ++h) {
+        if (h >= G) continue;
+        const float4 *ep = reinterpret_cast<const float4 *>(&W.p[h][0]);
+        float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+        for (int q4 = 0; q4 < kGroup / 4; ++q4) {
+            const float4 e4 = ep[q4];
+            const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t v = r.v[4 * q4 + u];
+                o0 = fmaf(ev[u], bf16_lo(v), o0);
+                o1 = fmaf(ev[u], bf16_hi(v), o1);
+            }
+        }
+        *reinterpret_cast<float2 *>(&sm.ro.o[h][2 * lane]) = make_float2(o0, o1);
+    }
+    KVQ_STAMP(13);
+}
+
+// The residual tokens' attention by the whole workgroup (every thread calls it; used when
+// the fused append completes a group, and written for a tile without a flush as well):
+//   1. V (and, with a flush, K) staged in LDS as binary32; the fused append's new token
+//      stored into its residual slot;
+//   2. flush: the 32 rows quantized into their page `flush_page` (same codec and bytes as
+//      kvq_append) and the tiles replaced by their dequantized values;
+//   3. scores: thread (token i / 16, channels 8 (i % 16) ..) against q~ (sm.qs), summed over
+//      the token's 16 lanes;
+//   4. softmax: one wave per head;
+//   5. values: thread (head, channel), a sum over the tokens in token order.
+// Returns false if the flush page id is outside the pool.
+template <int KB, int VB, int GS, int KM, int NW, int NT = 64 * NW>
+__device__ bool residual_wg(const DecodeParams &p, DecodeSmem<GS, KM, NW> &sm, const uint4 (&kv_in)[4 * (512 / NT)],
+                            int nres, int G, long long bh, bool append, bool flush, int flush_page)
+{
+    constexpr int KC = 512 / NT;
+    ResidualLds<GS> &R = sm.u.res;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    KVQ_STAMP(12);
+    // the chunks of the attended tokens: the new token's in row nres - 1 (fused append)
+    uint4 kv[2 * KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const int row = (tid + k * NT) / (kHeadDim / 8);
+        const bool fresh = append && row == nres - 1;
+        kv[k] = fresh ? kv_in[2 * KC + k] : kv_in[k];
+        kv[KC + k] = fresh ? kv_in[3 * KC + k] : kv_in[KC + k];
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const int i = tid + k * NT, row = i / (kHeadDim / 8), col = 8 * (i % (kHeadDim / 8));
         const uint32_t kw[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
-        const uint32_t vw[4] = {kv[2 + k].x, kv[2 + k].y, kv[2 + k].z, kv[2 + k].w};
+        const uint32_t vw[4] = {kv[KC + k].x, kv[KC + k].y, kv[KC + k].z, kv[KC + k].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            R.q.k[row * kTileStride + col + 2 * e] = __uint_as_float(kw[e] << 16);
-            R.q.k[row * kTileStride + col + 2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
-            R.q.v[row * kTileStride + col + 2 * e] = __uint_as_float(vw[e] << 16);
-            R.q.v[row * kTileStride + col + 2 * e + 1] = __uint_as_float(vw[e] & 0xFFFF0000u);
+            if (flush) {
+                R.q.k[row * kTileStride + col + 2 * e] = bf16_lo(kw[e]);
+                R.q.k[row * kTileStride + col + 2 * e + 1] = bf16_hi(kw[e]);
+            }
+            R.q.v[row * kTileStride + col + 2 * e] = bf16_lo(vw[e]);
+            R.q.v[row * kTileStride + col + 2 * e + 1] = bf16_hi(vw[e]);
         }
         if (append && row == nres - 1) {
             reinterpret_cast<uint4 *>(p.resid_k + bh * kGroup * kHeadDim)[i] = kv[k];
-            reinterpret_cast<uint4 *>(p.resid_v + bh * kGroup * kHeadDim)[i] = kv[2 + k];
+            reinterpret_cast<uint4 *>(p.resid_v + bh * kGroup * kHeadDim)[i] = kv[KC + k];
         }
     }
     __syncthreads();
@@ -521,43 +704,62 @@ __device__ bool residual_tokens(const DecodeParams &p, DecodeSmem<GS, KM> &sm, c
         }
         __syncthreads();
     }
-    // scores: thread (t, part) covers channels 16*part .. 16*part+15 of token t
-    {
-        const int t = tid >> 3, part = tid & 7;
-        for (int h = 0; h < G; ++h) {
-            float s = 0.0f;
-            if (t < nres) {
+    // scores
 #pragma unroll
-                for (int x = 0; x < 16; ++x) s = fmaf(sm.qs[h][16 * part + x], R.q.k[t * kTileStride + 16 * part + x], s);
+    for (int k = 0; k < KC; ++k) {
+        const int i = tid + k * NT, t = i / (kHeadDim / 8), part = i % (kHeadDim / 8);
+        float kf[8];
+        if (flush) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kf[e] = R.q.k[t * kTileStride + 8 * part + e];
+        } else {
+            const uint32_t kw[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kf[2 * e] = bf16_lo(kw[e]);
+                kf[2 * e + 1] = bf16_hi(kw[e]);
             }
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
-            s += __shfl_xor(s, 4);
+        }
+        for (int h = 0; h < G; ++h) {
+            const float4 qa = *reinterpret_cast<const float4 *>(&sm.qs[h][8 * part]);
+            const float4 qb = *reinterpret_cast<const float4 *>(&sm.qs[h][8 * part + 4]);
+            float s = qa.x * kf[0];
+            s = fmaf(qa.y, kf[1], s);
+            s = fmaf(qa.z, kf[2], s);
+            s = fmaf(qa.w, kf[3], s);
+            s = fmaf(qb.x, kf[4], s);
+            s = fmaf(qb.y, kf[5], s);
+            s = fmaf(qb.z, kf[6], s);
+            s = fmaf(qb.w, kf[7], s);
+            s = row_sum(s);                       // the token's 16 lanes
             if (part == 0) R.s[h][t] = t < nres ? s : -INFINITY;
         }
     }
     __syncthreads();
-    if (tid < G) {
-        const int h = tid;
-        float m = -INFINITY;
-        for (int t = 0; t < nres; ++t) m = fmaxf(m, R.s[h][t]);
-        float l = 0.0f;
-        for (int t = 0; t < kGroup; ++t) {
-            const float e = t < nres ? exp2f(R.s[h][t] - m) : 0.0f;
-            R.s[h][t] = e;
-            l += e;
+    // softmax over the tokens, one wave per head: lane t < 32 holds token t
+    for (int h = wave; h < G; h += NW) {
+        const float x = lane < kGroup ? R.s[h][lane] : -INFINITY;
+        const float mr = row_max(x);
+        const float m = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 0)),
+                              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 16)));
+        const float e = lane < nres ? __builtin_amdgcn_exp2f(x - m) : 0.0f;
+        const float er = row_sum(e);
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(er), 0)) +
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(er), 16));
+        if (lane < kGroup) R.s[h][lane] = e;
+        if (lane == 0) {
+            sm.ro.m[h] = m;
+            sm.ro.l[h] = l;
         }
-        sm.ro.m[h] = m;
-        sm.ro.l[h] = l;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
+    for (int idx = tid; idx < G * kHeadDim; idx += NT) {
         const int h = idx / kHeadDim, c = idx % kHeadDim;
         float o = 0.0f;
         for (int t = 0; t < nres; ++t) o = fmaf(R.s[h][t], R.q.v[t * kTileStride + c], o);
         sm.ro.o[h][c] = o;
     }
-    __syncthreads();
+    __syncthreads();     // the page loop reuses the space
     KVQ_STAMP(13);
     return ok;
 }
@@ -656,17 +858,50 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
     }
 }
 
+// Pages of a split among its waves, dealt in rounds, round r giving one page to every wave
+// whose weight exceeds r: weight 4 for every wave of an eight-wave workgroup but wave 0 of
+// split 0, which also attends the residual tokens and weighs 2 (a split of 64 pages: 8 per
+// wave, or on split 0 5, 9, 9, 9, 8, 8, 8, 8; the page loop's wave priorities balance the
+// two waves of each SIMD).  Four-wave workgroups (two per CU) deal one page per wave per
+// round.  Returns the split-relative index of the wave's page
+// `j` (increasing in j).
+template <int NW>
+__device__ __forceinline__ int page_weight(int w, int split)
+{
+    if constexpr (NW == 8) return w == 0 && split == 0 ? 2 : 4;
+    return 1;
+}
+
+template <int NW>
+__device__ __forceinline__ int split_page(int wave, int j, int split)
+{
+    int T = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) T += page_weight<NW>(v, split);
+    const int ww = page_weight<NW>(wave, split);
+    const int i = j % ww, cyc = j / ww;
+    int pos = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int v = 0; v < NW; ++v)
+            if (page_weight<NW>(v, split) > r && (r < i || (r == i && v < wave))) ++pos;
+    return cyc * T + pos;
+}
+
 // KM: the layer code -- integer codes with per-channel or per-token keys (one key group per
 // token and 32 channels), or FP8 / BF16 values
 // two waves per SIMD (two workgroups per CU) whenever G <= 8: at most 256 registers per lane
-template <int KB, int VB, int GS, typename QT, int KM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 2 ? 2 : 1))) void decode_kernel(DecodeParams p)
+template <int KB, int VB, int GS, typename QT, int KM, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(GS <= 2 ? 2 : 1)))
+void decode_kernel(DecodeParams p)
 {
+    constexpr int NT = 64 * NW;
     constexpr bool KT = KM == kLayerKeysPerToken;
     constexpr bool FLT = is_float_layer(KM);
     constexpr int kPageBytes = layer_page_bytes<KB, VB, KM>();
     constexpr int HS = 4 * GS;                 // head slots
-    __shared__ DecodeSmem<GS, KM> sm;
+    __shared__ DecodeSmem<GS, KM, NW> sm;
     // grid (H, batch, splits): the split index varies slowest, so every (sequence, KV head)
     // has its split 0 dispatched first
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
@@ -682,11 +917,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
     // lane-indexed vector load (lane i: sequence 64*(b/64) + i) and taken from lane b % 64: a
     // uniform scalar load would be waited for (with the kernel arguments) before the other
     // requests could go out -------------------------------------------------------------
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int a = lane >> 4, r16 = lane & 15;
     const int P = p.pages_per_split;
-    const int pg_begin = split * P + wave;
     const int pg_lim = min(p.max_pages, (split + 1) * P);    // >= 1
+    // the split-relative index of this lane's page (lane j: the wave's j-th page)
+    const int pg_rel = split_page<NW>(wave, lane, split);
     // lane roles in the page loop
     const int kq = lane >> 4, kjj = (lane >> 2) & 3, kj = lane & 3;   // key pair this lane folds
     // per-channel keys: any channel pair of the lane's 32-channel group; per-token keys: the
@@ -703,7 +939,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
     // last is issued; the length first, so that waiting for it leaves the others in flight)
     const int *len_src = append ? p.pos : p.seq_len;
     const int len_lane = len_src[min((b & ~63) + lane, p.batch - 1)];
-    const int bt_i = pg_begin + kWaves * lane;
+    const int bt_i = split * P + pg_rel;
     int my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + min(bt_i, pg_lim - 1)];
     // q straight from memory in the layouts the lane uses: 8 channels 8*r16 .. +7 of heads
     // 4i + a (the zero terms; their maxima give the per-head exponents) and channels ch0, ch1
@@ -739,7 +975,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
     if (bad_len || L == 0) {
         if (split == 0) {
             const float o = bad_len ? NAN : 0.0f;
-            for (int i = tid; i < G * kHeadDim; i += kThreads) out_bh[i] = o;
+            for (int i = tid; i < G * kHeadDim; i += NT) out_bh[i] = o;
             if (lse_bh && tid < G) lse_bh[tid] = bad_len ? NAN : -INFINITY;
         }
         KVQ_STAMP(5);
@@ -761,7 +997,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
     const bool has_res = nres > 0 && split == 0;
 
     const int pg_end = min(full, (split + 1) * P);
-    const int n_my = pg_begin < pg_end ? (pg_end - pg_begin + kWaves - 1) / kWaves : 0;
+    const int n_my = __builtin_popcountll(__ballot(bt_i < pg_end));
     // value pair this lane folds (group a): tokens (w, w+4) of its octet for 8-bit codes,
     // (w%2 + 4*(w/2), +2) for 2- and 4-bit codes, w = r16 % 4 -- the order their B operand
     // pairs take
@@ -770,11 +1006,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
     const int t1 = t0 + (VB == 8 ? 4 : 2);
     // powers of two the code unpack leaves on this lane's key channels / value tokens
     const int kshift = unpack_shift<KB>(kj), vshift = unpack_shift<VB>(r16 & 3);
-    // Everything requested so far (the length, the block-table ids, q) is in before the first
-    // page is requested: the memory counter completes in order, so a wait for q issued after
-    // the page requests would also wait for the page.  The q setup below then runs while the
-    // page is in flight.
-    __builtin_amdgcn_s_waitcnt(0);
+    // Without a flush, wave 0 of split 0 attends the residual tokens before its page loop:
+    // their rows are requested as soon as the length is known.  With a flush the workgroup
+    // quantizes and attends them after its page loop (rows requested after the first page).
+    const bool res_wave = has_res && !flush && wave == 0;
+    ResidualWaveRegs rw;
+    if (res_wave) load_residual_wave(p, bh, nres, append, rw);
+    // The first page is requested as soon as the block-table ids are in: q, requested before
+    // it, is waited for afterwards (the memory counter completes in order), which leaves the
+    // page in flight during the q setup below.
     const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
     // page ids outside the pool mark the sequence bad (NaN outputs) and are read as page 0
     const bool id_bad = lane < n_my && (my_phys < 0 || my_phys >= p.n_pages);
@@ -784,15 +1024,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
         const int phys = __builtin_amdgcn_readlane(my_phys, j);
         return pool + (static_cast<long long>(phys) * p.H + h) * kPageBytes;
     };
-    // the wave's first page and the residual rows go out as soon as the block-table ids are
-    // in, before the q setup below
     PageRegs<KB, VB> cur, nxt;
     if (n_my > 0) load_page<KB, VB, KM>(cur, page_base(0), lane, ch0, ch1, t0, t1);
-    uint4 res_kv[4];
-    if (has_res) load_residual(p, bh, nres, append, res_kv);
+    uint4 res_kv[4 * (512 / NT)];
+    if (has_res && flush) load_residual<NT>(p, bh, append, res_kv);
     KVQ_STAMP(9);
-    // q~ = q log2(e)/sqrt(128); the residual tokens (split 0, after the page loop) read it from
-    // LDS, written here by wave 0
+    // q~ = q log2(e)/sqrt(128); the residual tokens (split 0) read it from LDS, written here by
+    // wave 0
     if (wave == 0) {
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
@@ -817,18 +1055,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
         eqv[i] = 1 - e;
     }
     KVQ_STAMP(10);
+    if (res_wave) {
+        // (the highest issue priority while the other waves wait for their first pages)
+        if (NW == 8) __builtin_amdgcn_s_setprio(3);
+        wave_lds_sync();
+        residual_wave<GS, KM, NW>(p, sm, sm.u.w[0], rw, nres, G, bh, append);
+    }
 
     const long long slot0 = bh * p.n_splits;
     int early_cnt = -1;
     // ---- the split combine's batches of partials (splits s0 .. s0+kCB-1 of this (sequence,
     // KV head)): one thread per 4 consecutive channels of a head, kMI such items per thread
     constexpr int kVec = 4, kPerHead = kHeadDim / kVec;
-    constexpr int kMI = (HS * kPerHead + kThreads - 1) / kThreads;     // items per thread
+    constexpr int kMI = (HS * kPerHead + NT - 1) / NT;                 // items per thread
     constexpr int kCB = 4;
     float cmv[kMI][kCB], clv[kMI][kCB];
     float4 cov[kMI][kCB];
     auto load_batch = [&](int k, int s0) {
-        const int it = tid + k * kThreads;
+        const int it = tid + k * NT;
         const int hh = min(it / kPerHead, G - 1), c = (it % kPerHead) * kVec;
         const float *ml_base = p.part_ml + (slot0 * G + hh) * 2;            // split s at + s * G * 2
         const float *o_base = p.part_o + (slot0 * G + hh) * kHeadDim;       // split s at + s * G * 128
@@ -848,7 +1092,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
             }
         }
     };
-    if (tid == 0) sm.early = 0;
+    if (tid == 0) {
+        sm.early = 0;
+        sm.bad = 0;
+    }
     if (n_ps > 0) {
         WaveLds<GS, KM> &W = sm.u.w[wave];
         constexpr int NP = WaveLds<GS, KM>::NP, PG = WaveLds<GS, KM>::PG;
@@ -873,7 +1120,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
             }
             return x;
         };
-        float qw[HS][2];                                        // q~ of the folded key pair, every head
+        // q~ of the folded key pair, every head; per-channel integer keys keep it times
+        // 2^(KE - kshift), KE the wave's current key exponent (see the page work)
+        float qw[HS][2];
         float qb[GS][8];                                        // q~ of the zero-term channels
         float inv_eq[GS];                                       // 2^-eq of the lane's heads
 #pragma unroll
@@ -933,6 +1182,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
             wave_lds_sync();
         }
 
+        // per-channel integer keys: |q~ s 2^KE| < 2^15 for every channel of every page; KE is
+        // set from the first page and recomputed only for a page whose largest scale reaches
+        // 2^(14 - KE) or stays below 2^(6 - KE) (thresholds ke_hi / ke_lo, 0 before the first
+        // page), where sck = 2^-KE / 2^eq undoes it in the scores
+        int KE = 0;
+        uint32_t ke_hi = 0u, ke_lo = 0u;
+        float sck[GS];
+#pragma unroll
+        for (int i = 0; i < GS; ++i) sck[i] = inv_eq[i];
+        if constexpr (!KT && !FLT) {
+#pragma unroll
+            for (int hh = 0; hh < HS; ++hh) {
+                qw[hh][0] = ldexpf(qw[hh][0], -kshift);
+                qw[hh][1] = ldexpf(qw[hh][1], -kshift);
+            }
+        }
         const uint32_t magic = fp16x2_1024();
         float4_t acc[8];
 #pragma unroll
@@ -950,8 +1215,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
             for (int j = 0; j < 4; ++j) zb[i][j] = 0.0f;
         // The value accumulators hold sum_t (p s 2^ev) v: ev keeps the folded
         // weights in the normal fp16 range (|p s 2^ev| < 2^15); it only decreases, rescaling
-        // acc when it does.
+        // acc when it does -- exactly when a page holds a scale >= 2^(14 - ev) (threshold
+        // ev_thr); fv = 2^(ev - vshift) scales this lane's weights before the fold.
         int ev = 127;
+        uint32_t ev_thr = 1u;
+        float fv = ldexpf(1.0f, ev - vshift);
 
         auto process_page = [&](const PageRegs<KB, VB> &cur) {
           float s2[2][GS];
@@ -985,27 +1253,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) s2[blk][i] = dsum(sacc[blk], i) * ksc[i];
           } else if constexpr (!KT) {
-            // ---- page exponent: |q~ s 2^E| < 2^15 for every channel ---------------
-            uint32_t smax = 0;
+            // ---- key exponent: every lane checks the two scales it folds; the exact page
+            // exponent (the largest scale of the page) only when one is out of range ---------
+            {
+                // (the barrier keeps the compiler from moving the masks up to the loads, where
+                // they would wait for a page just requested)
+                uint32_t kw0 = cur.kszw[0], kw1 = cur.kszw[1];
+                __asm__ volatile("" : "+v"(kw0), "+v"(kw1));
+                const uint32_t u = max(kw0 & 0xFFFFu, kw1 & 0xFFFFu);
+                if (__any(u >= ke_hi) || !__any(u >= ke_lo)) {
+                    uint32_t smax = 0;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) smax = max(smax, cur.kszb[x] & 0x7FFFu);
-            smax = row_max_u32(smax);
-            int E = 0;
-            if (smax != 0u) {
-                int e;
-                frexpf(half_bits_to_float(smax), &e);
-                E = 14 - e;
+                    for (int x = 0; x < 8; ++x) smax = max(smax, cur.kszb[x] & 0x7FFFu);
+                    smax = row_max_u32(smax);
+                    int E = 0;
+                    if (smax != 0u) {
+                        int e;
+                        frexpf(half_bits_to_float(smax), &e);
+                        E = 14 - e;
+                    }
+#pragma unroll
+                    for (int hh = 0; hh < HS; ++hh) {
+                        qw[hh][0] = ldexpf(qw[hh][0], E - KE);
+                        qw[hh][1] = ldexpf(qw[hh][1], E - KE);
+                    }
+#pragma unroll
+                    for (int i = 0; i < GS; ++i) sck[i] = ldexpf(inv_eq[i], -E);
+                    KE = E;
+                    ke_hi = fp16_pow2_bits(14 - KE);
+                    ke_lo = 14 - KE - 8 < -24 ? 0u : fp16_pow2_bits(14 - KE - 8);
+                }
             }
             // ---- fold key scales into q: two channels x every head slot, hi/lo ---------
-            {
-                const float s0 = ldexpf(half_bits_to_float(cur.kszw[0] & 0xFFFFu), E - kshift);
-                const float s1 = ldexpf(half_bits_to_float(cur.kszw[1] & 0xFFFFu), E - kshift);
 #pragma unroll
-                for (int hh = 0; hh < HS; ++hh) {
-                    const uint32_t hi = split_hi(qw[hh][0] * s0, qw[hh][1] * s1);
-                    W.qp[0][hh][lane] = hi;
-                    W.qp[1][hh][lane] = split_lo(qw[hh][0], s0, qw[hh][1], s1, hi);
-                }
+            for (int hh = 0; hh < HS; ++hh) {
+                const uint32_t hi = fold_hi(qw[hh][0], qw[hh][1], cur.kszw[0], cur.kszw[1]);
+                W.qp[0][hh][lane] = hi;
+                W.qp[1][hh][lane] = fold_lo(qw[hh][0], qw[hh][1], cur.kszw[0], cur.kszw[1], hi);
             }
             // ---- key zero terms: sum_c q~_c z_c per head, lane group a holds heads a+4i
             float bias[GS];
@@ -1030,13 +1314,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
                     if constexpr (!RS) sacc[blk] = mfma(alo, bk, sacc[blk]);
                 }
             }
-            const float sce = ldexpf(1.0f, -E);
 #pragma unroll
             for (int i = 0; i < GS; ++i) {
-                const float sc = sce * inv_eq[i];
                 const float bc = bias[i] * inv_eq[i];
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = fmaf(dsum(sacc[blk], i), sc, bc);
+                for (int blk = 0; blk < 2; ++blk) s2[blk][i] = fmaf(dsum(sacc[blk], i), sck[i], bc);
             }
           } else {
             // ---- per-token keys: one accumulator per key group, then the token's scales --
@@ -1139,40 +1421,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
                 }
             }
           } else {
-            // ---- value-scale exponent of this page -----------------------------------
+            // ---- value-scale exponent: ev decreases when a page holds a scale >= 2^(14 - ev)
+            // (a check of the lane's own eight scales); the page's exact exponent only then
             {
-                // every row of lanes holds all 32 tokens and all four groups
-                uint32_t vmax = 0;
+                uint32_t vw[2][4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) vmax = max(vmax, max(cur.vszq[0][j] & 0x7FFFu, cur.vszq[1][j] & 0x7FFFu));
-                vmax = row_max_u32(vmax);
-                if (vmax != 0u) {
-                    int e;
-                    frexpf(half_bits_to_float(vmax), &e);
-                    const int ev_page = 14 - e;
-                    if (ev_page < ev) {
-                        const float f = ldexpf(1.0f, ev_page - ev);
+                for (int j = 0; j < 4; ++j) {
+                    vw[0][j] = cur.vszq[0][j];
+                    vw[1][j] = cur.vszq[1][j];
+                }
+                __asm__ volatile("" : "+v"(vw[0][0]), "+v"(vw[0][1]), "+v"(vw[0][2]), "+v"(vw[0][3]),
+                                      "+v"(vw[1][0]), "+v"(vw[1][1]), "+v"(vw[1][2]), "+v"(vw[1][3]));
+                uint32_t u = 0;
 #pragma unroll
-                        for (int nb = 0; nb < 8; ++nb) acc[nb] *= f;
-                        ev = ev_page;
+                for (int j = 0; j < 4; ++j) u = max(u, max(vw[0][j] & 0xFFFFu, vw[1][j] & 0xFFFFu));
+                if (__any(u >= ev_thr)) {
+                    // every row of lanes holds all 32 tokens and all four groups
+                    uint32_t vmax = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vmax = max(vmax, max(cur.vszq[0][j] & 0x7FFFu, cur.vszq[1][j] & 0x7FFFu));
+                    vmax = row_max_u32(vmax);
+                    if (vmax != 0u) {
+                        int e;
+                        frexpf(half_bits_to_float(vmax), &e);
+                        const int ev_page = 14 - e;
+                        if (ev_page < ev) {
+                            const float f = ldexpf(1.0f, ev_page - ev);
+#pragma unroll
+                            for (int nb = 0; nb < 8; ++nb) acc[nb] *= f;
+                            ev = ev_page;
+                            ev_thr = fp16_pow2_bits(14 - ev);
+                            fv = ldexpf(1.0f, ev - vshift);
+                        }
                     }
                 }
             }
             // ---- fold value scales into p: the lane's own weights of tokens t0, t1 x every
             // value group, hi/lo (no exchange: the scores put this lane's pair in its registers)
+            float ps[2][GS];
+#pragma unroll
+            for (int i = 0; i < GS; ++i) {
+                ps[0][i] = pw[0][i] * fv;
+                ps[1][i] = pw[1][i] * fv;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float sv0 = ldexpf(half_bits_to_float(cur.vszq[0][j] & 0xFFFFu), ev - vshift);
-                const float sv1 = ldexpf(half_bits_to_float(cur.vszq[1][j] & 0xFFFFu), ev - vshift);
-                const float zv0 = half_bits_to_float(cur.vszq[0][j] >> 16);
-                const float zv1 = half_bits_to_float(cur.vszq[1][j] >> 16);
+                const uint32_t w0 = cur.vszq[0][j], w1 = cur.vszq[1][j];
 #pragma unroll
                 for (int i = 0; i < GS; ++i) {
-                    const float p0 = pw[0][i], p1 = pw[1][i];
-                    const uint32_t hi = split_hi(p0 * sv0, p1 * sv1);
+                    const uint32_t hi = fold_hi(ps[0][i], ps[1][i], w0, w1);
                     W.pp_row(j, 0, 4 * i + a)[r16] = hi;
-                    W.pp_row(j, 1, 4 * i + a)[r16] = split_lo(p0, sv0, p1, sv1, hi);
-                    zb[i][j] = fmaf(p0, zv0, fmaf(p1, zv1, zb[i][j]));
+                    W.pp_row(j, 1, 4 * i + a)[r16] = fold_lo(ps[0][i], ps[1][i], w0, w1, hi);
+                    zb[i][j] = fmaf(pw[0][i], static_cast<float>(hi_half(w0)),
+                                    fmaf(pw[1][i], static_cast<float>(hi_half(w1)), zb[i][j]));
                 }
             }
             wave_lds_sync();
@@ -1197,18 +1498,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
         auto prefetch = [&](PageRegs<KB, VB> &dst, int j) {
             load_page<KB, VB, KM>(dst, page_base(min(j, n_my - 1)), lane, ch0, ch1, t0, t1);
         };
+        // The two waves of a SIMD share its issue arbiter, which favours the higher priority and
+        // then the older wave: each wave's priority follows the pages it has left, so the wave
+        // that is behind is served first and the two run out of pages together.
+        auto set_prio = [&](int left) {
+            if (NW != 8) return;
+            if (left > 6) __builtin_amdgcn_s_setprio(3);
+            else if (left > 4) __builtin_amdgcn_s_setprio(2);
+            else if (left > 2) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        };
         KVQ_STAMP(1);
         int j = 0;
         for (; j + 1 < n_my; j += 2) {
             prefetch(nxt, j + 1);
+            set_prio(n_my - j);
             process_page(cur);
             if (j == 0) KVQ_STAMP(11);
             prefetch(cur, j + 2);
+            set_prio(n_my - j - 1);
             process_page(nxt);
         }
-        if (j < n_my) process_page(cur);
+        if (j < n_my) {
+            set_prio(1);
+            process_page(cur);
+        }
+        if (NW == 8) __builtin_amdgcn_s_setprio(0);
         KVQ_STAMP(2);
-        // the split counter, read early: used after the merge barrier (see the merge below)
+        // the split counter, read right after the page loop and used after the merge (see below)
         if (tid == 0 && n_work > 1) early_cnt = __hip_atomic_load(p.counters + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
         // ---- this wave's state: l per head, value zero terms, unnormalized output -------
@@ -1240,13 +1557,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
 #pragma unroll
                 for (int i = 0; i < GS; ++i) o_out[nb][i] = fmaf(dsum(acc[nb], i), unscale, W.bv[nb >> 1][4 * i + a]);
         }
-        // Thread 0 read the split counter right after its page loop (early_cnt).  When every
-        // other split of this (sequence, KV head) had published its partial by then, this
-        // workgroup combines at once, with its own state from registers, and publishes nothing.
-        if (tid == 0) sm.early = n_work > 1 && early_cnt == n_work - 1;
         __syncthreads();     // every wave is done with its WaveLds: reuse the space
-        if (has_res) bad_page |= !residual_tokens<KB, VB, GS, KM>(p, sm, res_kv, nres, G, bh, append, flush, full);
-        MergeLds<GS> &M = sm.u.merge;
+        KVQ_STAMP(14);
+        if (has_res && flush)
+            bad_page |= !residual_wg<KB, VB, GS, KM, NW>(p, sm, res_kv, nres, G, bh, append, flush, full);
+        MergeLds<GS, NW> &M = sm.u.merge;
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
             const int hh = 4 * i + a;
@@ -1259,23 +1574,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
                 }
             }
         }
-    } else if (has_res) {
-        bad_page |= !residual_tokens<KB, VB, GS, KM>(p, sm, res_kv, nres, G, bh, append, flush, full);
+    } else if (has_res && flush) {
+        bad_page |= !residual_wg<KB, VB, GS, KM, NW>(p, sm, res_kv, nres, G, bh, append, flush, full);
     }
 
     // ---- this workgroup's merge: its waves' page states and, on split 0, the residual ----
-    const bool bad = __syncthreads_or(bad_page);
+    // (bad_page is uniform in each wave: any wave that has it set marks the workgroup; one
+    // barrier, where a block-wide OR would take three)
+    if (bad_page && lane == 0) sm.bad = 1;
+    __syncthreads();
+    const bool bad = sm.bad != 0;
+    KVQ_STAMP(15);
     const bool single = n_work == 1;
-    const bool early = sm.early != 0;
     // one thread per 4 consecutive channels of a head: the head's weights once, then 16-byte
     // reads of the waves' partial outputs (exponents <= 0: the raw exp2)
     float om[kMI], ol[kMI];
     float4 oo[kMI];
     {
-        const MergeLds<GS> &M = sm.u.merge;
+        const MergeLds<GS, NW> &M = sm.u.merge;
 #pragma unroll
         for (int k = 0; k < kMI; ++k) {
-            const int it = tid + k * kThreads;
+            const int it = tid + k * NT;
             om[k] = -INFINITY;
             ol[k] = 0.0f;
             oo[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -1284,7 +1603,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
             float m = has_res ? sm.ro.m[hh] : -INFINITY;
             if (n_ps > 0) {
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) m = fmaxf(m, M.m[w][hh]);
+                for (int w = 0; w < NW; ++w) m = fmaxf(m, M.m[w][hh]);
             }
             float l = 0.0f;
             float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -1296,7 +1615,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
             }
             if (n_ps > 0) {
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
+                for (int w = 0; w < NW; ++w) {
                     const float wt = M.m[w][hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M.m[w][hh] - m);
                     const float4 r = *reinterpret_cast<const float4 *>(&M.o[w][hh][c]);
                     l = fmaf(wt, M.l[w][hh], l);
@@ -1312,7 +1631,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
     if (single) {
 #pragma unroll
         for (int k = 0; k < kMI; ++k) {
-            const int it = tid + k * kThreads;
+            const int it = tid + k * NT;
             if (it >= G * kPerHead) continue;
             const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
             const float inv = 1.0f / ol[k];
@@ -1324,12 +1643,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
         KVQ_STAMP(5);
         return;
     }
+    // Thread 0 read the split counter right after its page loop (early_cnt, used only now: its
+    // latency passes under the merge).  When every other split of this (sequence, KV head)
+    // had published its partial by then, this workgroup combines at once, with its own state
+    // from registers, and publishes nothing.
+    if (tid == 0 && early_cnt >= 0) sm.early = early_cnt == n_work - 1;
+    __syncthreads();
+    const bool early = sm.early != 0;
     if (!early) {
         // publish (m, l, o) with device-scope stores, wait until they are complete, then count
         // this split in; the workgroup that completes the count combines
 #pragma unroll
         for (int k = 0; k < kMI; ++k) {
-            const int it = tid + k * kThreads;
+            const int it = tid + k * NT;
             if (it >= G * kPerHead) continue;
             const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
             float *po = p.part_o + ((slot0 + split) * G + hh) * kHeadDim;
@@ -1366,7 +1692,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GS <= 
     // own partial comes from registers.
 #pragma unroll
     for (int k = 0; k < kMI; ++k) {
-        const int it = tid + k * kThreads;
+        const int it = tid + k * NT;
         if (it >= G * kPerHead) continue;
         const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
         const float *ml_base = p.part_ml + (slot0 * G + hh) * 2;
@@ -1419,23 +1745,24 @@ __global__ void zero_fill_kernel(uint32_t *p, size_t n_words)
 }
 #endif
 
-template <int KB, int VB, int GS, int KM>
+template <int KB, int VB, int GS, int KM, int NW>
 hipError_t launch_decode_g(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
     dim3 grid(p.H, p.batch, p.n_splits);
     if (q_f32)
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float, KM>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float, KM, NW>), grid, dim3(64 * NW), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t, KM>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t, KM, NW>), grid, dim3(64 * NW), 0, s, p);
     return hipGetLastError();
 }
 
 template <int KB, int VB, int KM>
 hipError_t launch_decode_k(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
-    if (p.G <= 4) return launch_decode_g<KB, VB, 1, KM>(p, q_f32, s);
-    if (p.G <= 8) return launch_decode_g<KB, VB, 2, KM>(p, q_f32, s);
-    return launch_decode_g<KB, VB, 4, KM>(p, q_f32, s);
+    const bool w8 = p.waves == 8;
+    if (p.G <= 4) return w8 ? launch_decode_g<KB, VB, 1, KM, 8>(p, q_f32, s) : launch_decode_g<KB, VB, 1, KM, 4>(p, q_f32, s);
+    if (p.G <= 8) return w8 ? launch_decode_g<KB, VB, 2, KM, 8>(p, q_f32, s) : launch_decode_g<KB, VB, 2, KM, 4>(p, q_f32, s);
+    return launch_decode_g<KB, VB, 4, KM, 4>(p, q_f32, s);
 }
 
 // integer layers: key mode 0 / 1
@@ -1485,15 +1812,22 @@ DecodeWorkspace decode_workspace_layout(int batch, int H, int G, int n_splits)
     return w;
 }
 
-int decode_default_pages_per_split(int batch, int H, int max_full_pages)
+int decode_waves_for(int batch, int H, int G)
 {
-    // about 512 workgroups of four waves for the longest sequences (two per CU resident at
-    // once), at least four pages per wave, at most 64 per wave (block-table ids are held
-    // one per lane)
+    return G <= 8 && static_cast<long long>(batch) * H <= 256 ? 8 : 4;
+}
+
+int decode_default_pages_per_split(int batch, int H, int G, int max_full_pages)
+{
+    // about 2048 waves for the longest sequences (eight per CU, all resident at once), at
+    // least four pages per wave, at most 256 pages per split (32 or 64 per wave: block-table
+    // ids are held one per lane)
+    const int nw = decode_waves_for(batch, H, G);
+    const long long wgs = 2048 / nw;
     const long long work = static_cast<long long>(batch) * H * (max_full_pages > 0 ? max_full_pages : 1);
-    long long pps = (work + 511) / 512;
-    pps = (pps + kWaves - 1) / kWaves * kWaves;
-    if (pps < 4 * kWaves) pps = 4 * kWaves;
+    long long pps = (work + wgs - 1) / wgs;
+    pps = (pps + nw - 1) / nw * nw;
+    if (pps < 4 * nw) pps = 4 * nw;
     if (pps > 256) pps = 256;
     return static_cast<int>(pps);
 }

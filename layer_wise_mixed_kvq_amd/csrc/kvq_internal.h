@@ -61,6 +61,7 @@ struct DecodeParams {
     int max_seq_len;
     int pages_per_split;
     int n_splits;         // page splits per (b, h)
+    int waves;            // waves per workgroup: 8 or 4 (decode_waves_for)
     // profiling build only (KVQ_PHASE_TIMERS): per wave, [kPhaseStamps] u64 real-time
     // stamps at the kernel's phase boundaries; null otherwise
     unsigned long long *phase_ts;
@@ -68,9 +69,9 @@ struct DecodeParams {
 
 // Phase-timer record per wave (KVQ_PHASE_TIMERS builds): stamps 0-5 are the 100 MHz
 // real-time counter at entry, page loop start, page loop end, partials stored, split
-// counter known, exit; stamps 8-13 at finer points: length known, q staged (first barrier),
-// q exponents (second barrier), first page done, residual tokens start and end (0 where
-// a wave did not reach the point).  Stamp 6 holds the hardware XCC id (bits 32-35) and
+// counter known, exit; stamps 8-13 at finer points: length known, first page requested, q
+// setup done, first page done, residual tokens start and end; 14 and 15 after the two
+// barriers of the workgroup's merge (0 where a wave did not reach the point).  Stamp 6 holds the hardware XCC id (bits 32-35) and
 // HW_ID register (bits 0-31); stamp 7 the work item as h | b << 20 | split << 40.
 constexpr int kPhaseStamps = 16;
 #if defined(KVQ_PHASE_TIMERS)
@@ -83,7 +84,8 @@ struct DecodeWorkspace {
     size_t part_o_off, part_ml_off, counters_off, bytes;
 };
 DecodeWorkspace decode_workspace_layout(int batch, int H, int G, int n_splits);
-int decode_default_pages_per_split(int batch, int H, int max_full_pages);
+int decode_waves_for(int batch, int H, int G);
+int decode_default_pages_per_split(int batch, int H, int G, int max_full_pages);
 
 // kmode: the layer code -- 0 = integer codes with per-channel keys, 1 = integer codes with
 // per-token keys, 2 = FP8 E4M3 (kb = vb = 8), 3 = BF16 (kb = vb = 16)
@@ -101,7 +103,7 @@ hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t s);
 
 #if defined(KVQ_PHASE_TIMERS)
 // Profiling build only (libkvq_phases.so): every later decode launch whose per-wave
-// records ([H][batch][splits][4 waves][kPhaseStamps] u64) fit in `bytes` writes them to
+// records ([H][batch][splits][8 wave slots][kPhaseStamps] u64) fit in `bytes` writes them to
 // the device buffer `buf`; null turns the recording off.
 extern "C" void kvq_profile_set_phase_buffer(void *buf, size_t bytes);
 #endif

@@ -139,9 +139,10 @@ def traffic_md(rec: dict) -> str:
     return "\n".join(lines) + "\n"
 
 
-PHASE_NAMES = {0: "entry", 8: "length known", 9: "q staged (barrier 1)", 10: "q exponents (barrier 2)",
+PHASE_NAMES = {0: "entry", 8: "length known", 9: "first page requested", 10: "q setup done",
                1: "page loop start", 11: "first page done", 2: "page loop end", 12: "residual start",
-               13: "residual end", 3: "partials stored", 4: "split counter known", 5: "exit"}
+               13: "residual end", 14: "merge barrier 1", 15: "merge barrier 2", 3: "partials stored",
+               4: "split counter known", 5: "exit"}
 N_STAMPS = 16
 
 
@@ -178,6 +179,33 @@ def phase_summary(rec) -> dict:
             v = rel(2)[sel & (split == sp)]
             by[int(sp)] = float(np.median(v))
         out["page_loop_end_median_by_split_us"] = by
+    # sharing of compute units: waves of one CU (XCC id and HW_ID bits 8..15: CU, shader
+    # array, shader engine), their workgroups in order of entry, and how far apart the page
+    # loops of a CU's workgroups end
+    cu = ((live[:, 6] >> 32) & 0xF).astype(np.int64) * 256 + ((live[:, 6] >> 8) & 0xFF).astype(np.int64)
+    wg = (live[:, 7]).astype(np.int64)
+    spread, first_last, wgs_per_cu = [], [], []
+    for c in np.unique(cu):
+        m = (cu == c) & sel
+        if not m.any():
+            continue
+        ends = {}
+        ent = {}
+        for w_, e_, t_ in zip(wg[m], rel(2)[m], rel(0)[m]):
+            ends[w_] = max(ends.get(w_, 0.0), e_)
+            ent[w_] = min(ent.get(w_, 1e9), t_)
+        order = sorted(ends, key=lambda k: ent[k])
+        wgs_per_cu.append(len(order))
+        spread.append(float(rel(2)[m].max() - rel(2)[m].min()))
+        if len(order) >= 2:
+            first_last.append((ends[order[0]], ends[order[-1]]))
+    out["cus"] = {"n": len(spread), "workgroups_per_cu": {int(k): int(v) for k, v in
+                                                          zip(*np.unique(wgs_per_cu, return_counts=True))},
+                  "loop_end_spread_within_cu_median_us": float(np.median(spread)) if spread else None}
+    if first_last:
+        fl = np.array(first_last)
+        out["cus"]["loop_end_first_vs_last_entered_wg_median_us"] = [float(np.median(fl[:, 0])),
+                                                                    float(np.median(fl[:, 1]))]
     # XCD placement: does every (sequence, KV head) keep all its splits on one XCD?
     xcc = ((live[:, 6] >> 32) & 0xF).astype(np.int64)
     item = (live[:, 7] & ((1 << 40) - 1)).astype(np.int64)
@@ -201,6 +229,14 @@ def phases_md(summ: dict, cmd: str, title: str) -> str:
     if "page_loop_end_median_by_split_us" in summ:
         lines += ["", "Page loop end, median by split index (us): " +
                   ", ".join(f"{k}: {v:.2f}" for k, v in summ["page_loop_end_median_by_split_us"].items())]
+    if "cus" in summ:
+        c = summ["cus"]
+        lines += ["", f"Compute units used: {c['n']}; workgroups per CU: {c['workgroups_per_cu']}; page-loop end "
+                  f"spread within a CU (median over CUs): {c['loop_end_spread_within_cu_median_us']:.2f} us" +
+                  (f"; loop end of the first- and last-entered workgroup of a CU (medians): "
+                   f"{c['loop_end_first_vs_last_entered_wg_median_us'][0]:.2f} / "
+                   f"{c['loop_end_first_vs_last_entered_wg_median_us'][1]:.2f} us"
+                   if "loop_end_first_vs_last_entered_wg_median_us" in c else "")]
     x = summ["xcds"]
     lines += ["", "Waves per XCD: " + ", ".join(f"{k}: {v}" for k, v in x["waves_per_xcd"].items()) +
               f"; every (sequence, KV head) on one XCD: {x['every_item_on_one_xcd']}"]
@@ -223,7 +259,7 @@ def phases(args) -> str:
     import bench
     cfg = bench.CONFIGS[args.config]
     stack = bench.DecodeStack(cfg, "cuda")
-    n_rec = stack.H * stack.B * stack.max_pages * 4
+    n_rec = stack.H * stack.B * stack.max_pages * 8          # >= workgroups x 8 wave slots
     buf = torch.zeros(n_rec * N_STAMPS, dtype=torch.int64, device="cuda")
     kvq = stack.kvq
 
@@ -252,10 +288,13 @@ def phases(args) -> str:
         g.replay()
         torch.cuda.synchronize()
         rec = buf.view(-1, N_STAMPS).cpu().numpy().view(np.uint64)
-        summaries.append(phase_summary(rec))
+        summaries.append((phase_summary(rec), rec.copy()))
     # the replay with the median exit time
-    summaries.sort(key=lambda s_: s_["phases"]["exit"]["max_us"])
-    summ = summaries[len(summaries) // 2]
+    summaries.sort(key=lambda s_: s_[0]["phases"]["exit"]["max_us"])
+    summ, raw = summaries[len(summaries) // 2]
+    if args.raw:
+        np.save(args.raw, raw[raw[:, 0] != 0])
+    summaries = [s_ for s_, _ in summaries]
     kb, vb = cfg["pairs"][args.layer] if not isinstance(cfg["pairs"][args.layer], str) else (0, 0)
     title = (f"{cfg['workload']}, layer {args.layer} ({cfg['pairs'][args.layer]}); median of {args.reps} graph "
              "replays of the whole step by last exit")
@@ -302,6 +341,7 @@ def main(argv=None):
     ph.add_argument("--lib", help="another phase-timer build of the library to load")
     ph.add_argument("--touch-stride", type=int, default=0,
                     help="before the layer's launch, read one byte per this many bytes of its pool, q and out")
+    ph.add_argument("--raw", help="also save that replay's per-wave records (.npy, uint64 [waves][16])")
     ph.add_argument("--out")
     a = ap.parse_args(argv)
     if a.what == "stats":

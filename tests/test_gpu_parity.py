@@ -78,6 +78,41 @@ def test_decode_parity(kvq, orc, kb, vb, G):
     assert_attention_close(out, lse, o_ref, l_ref, f"kb={kb} vb={vb} G={G}")
 
 
+@pytest.mark.parametrize("G", [4, 7])
+def test_decode_four_wave_workgroups(kvq, orc, G):
+    """More than 256 (sequence, KV head) pairs with G <= 8: the launch takes four-wave
+    workgroups (two per CU) instead of eight; plain decode and the fused append, several
+    split sizes, lengths with no full page, a ragged tail or a page about to complete."""
+    import torch
+    import synth
+    H, B = 8, 36
+    rng = np.random.default_rng(G)
+    L0 = rng.integers(1, 200, B).astype(np.int32)
+    L0[:4] = [1, 31, 63, 95]
+    c = Case(4, 2, H=H, G=G, lens=list(L0 + 1), seed=300 + G)
+    log(f"four-wave workgroups: B={B} H={H} G={G}")
+    c.o_pages, c.o_rk, c.o_rv = orc.new_cache(4, 2, H, B, c.n_phys)
+    orc.pack(4, 2, host_array(c.k), host_array(c.v), L0, c.bt, c.o_pages, c.o_rk, c.o_rv)
+    c.device_setup(kvq)
+    l0 = torch.from_numpy(L0).to(c.dev)
+    kvq.kvq_pack(c.model, 0, c.cache, c.k.to(c.dev), c.v.to(c.dev), l0)
+    q = c.q.to(c.dev)
+    msl = c.maxp * 32
+    o_ref, l_ref = orc.decode_attn(4, 2, H, host_array(c.q), L0, c.bt, c.o_pages, c.o_rk, c.o_rv)
+    for pps in (0, 1, 3):
+        out, lse = kvq.kvq_decode_attn(c.model, 0, c.cache, q, l0, msl, pages_per_split=pps)
+        assert_attention_close(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"decode pps={pps}")
+    kn = synth.fill(c.seed, synth.KIND_K_NEW, 0, B, 1, H).view(B, H, 128)
+    vn = synth.fill(c.seed, synth.KIND_V_NEW, 0, B, 1, H).view(B, H, 128)
+    orc.append(4, 2, host_array(kn), host_array(vn), L0, c.bt, c.o_pages, c.o_rk, c.o_rv)
+    o_ref, l_ref = orc.decode_attn(4, 2, H, host_array(c.q), L0 + 1, c.bt, c.o_pages, c.o_rk, c.o_rv)
+    out, lse = kvq.kvq_append_decode_attn(c.model, 0, c.cache, kn.to(c.dev), vn.to(c.dev), l0, q, msl,
+                                          pages_per_split=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cache.pages.cpu().numpy(), c.o_pages), "pages after the fused append differ"
+    assert_attention_close(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "fused")
+
+
 @pytest.mark.parametrize("q_dtype", ["bf16", "f32"])
 def test_decode_q_dtypes(kvq, orc, q_dtype):
     c = Case(4, 2, H=2, G=4, lens=[300, 64], seed=77, q_dtype=q_dtype)

@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     # MFMA accumulators in ordinary VGPRs: the decode kernel rescales them with VALU ops,
     # and the AGPR form would copy them across the register files around every MFMA
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # leading scalar kernel arguments (the decode kernel's prologue fields) preloaded into
+    # scalar registers by the dispatch
+    "-mllvm", "-amdgpu-kernarg-preload-count=10",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -863,30 +863,17 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
 // split 0, which also attends the residual tokens and weighs 2 (a split of 64 pages: 8 per
 // wave, or on split 0 5, 9, 9, 9, 8, 8, 8, 8; the page loop's wave priorities balance the
 // two waves of each SIMD).  Four-wave workgroups (two per CU) deal one page per wave per
-// round.  Returns the split-relative index of the wave's page
-// `j` (increasing in j).
-template <int NW>
-__device__ __forceinline__ int page_weight(int w, int split)
-{
-    if constexpr (NW == 8) return w == 0 && split == 0 ? 2 : 4;
-    return 1;
-}
-
+// round.  Returns the split-relative index of the wave's page `j` (increasing in j), in
+// closed form: on split 0 a cycle of four rounds deals 30 pages, rounds 0 and 1 to all eight
+// waves, rounds 2 and 3 to waves 1-7.
 template <int NW>
 __device__ __forceinline__ int split_page(int wave, int j, int split)
 {
-    int T = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) T += page_weight<NW>(v, split);
-    const int ww = page_weight<NW>(wave, split);
-    const int i = j % ww, cyc = j / ww;
-    int pos = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int v = 0; v < NW; ++v)
-            if (page_weight<NW>(v, split) > r && (r < i || (r == i && v < wave))) ++pos;
-    return cyc * T + pos;
+    if constexpr (NW != 8) return NW * j + wave;
+    if (split != 0) return 8 * j + wave;
+    if (wave == 0) return 30 * (j >> 1) + 8 * (j & 1);
+    const int i = j & 3;
+    return 30 * (j >> 2) + (i < 2 ? 8 * i + wave : 16 + 7 * (i - 2) + wave - 1);
 }
 
 // KM: the layer code -- integer codes with per-channel or per-token keys (one key group per
@@ -894,7 +881,8 @@ __device__ __forceinline__ int split_page(int wave, int j, int split)
 // two waves per SIMD (two workgroups per CU) whenever G <= 8: at most 256 registers per lane
 template <int KB, int VB, int GS, typename QT, int KM, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(GS <= 2 ? 2 : 1)))
-void decode_kernel(DecodeParams p)
+void decode_kernel(const int32_t *len_src, const int32_t *block_table, const void *q_in, const uint8_t *pool,
+                   int batch, int max_pages, int P, int H, int G, int fused, DecodeParams p)
 {
     constexpr int NT = 64 * NW;
     constexpr bool KT = KM == kLayerKeysPerToken;
@@ -906,12 +894,11 @@ void decode_kernel(DecodeParams p)
     // has its split 0 dispatched first
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x;
-    const int G = p.G;
     KVQ_STAMP(0);
-    const long long bh = static_cast<long long>(b) * p.H + h;
+    const long long bh = static_cast<long long>(b) * H + h;
     float *out_bh = p.out + bh * G * kHeadDim;
     float *lse_bh = p.lse ? p.lse + bh * G : nullptr;
-    const bool append = p.pos != nullptr;      // fused append: attend over pos + 1 tokens
+    const bool append = fused != 0;            // fused append: attend over pos + 1 tokens
     // ---- the length, this wave's block-table ids (every page the split could hold) and q
     // are requested together, before any of them is waited for.  The length is read as a
     // lane-indexed vector load (lane i: sequence 64*(b/64) + i) and taken from lane b % 64: a
@@ -919,8 +906,7 @@ void decode_kernel(DecodeParams p)
     // requests could go out -------------------------------------------------------------
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int a = lane >> 4, r16 = lane & 15;
-    const int P = p.pages_per_split;
-    const int pg_lim = min(p.max_pages, (split + 1) * P);    // >= 1
+    const int pg_lim = min(max_pages, (split + 1) * P);    // >= 1
     // the split-relative index of this lane's page (lane j: the wave's j-th page)
     const int pg_rel = split_page<NW>(wave, lane, split);
     // lane roles in the page loop
@@ -937,10 +923,9 @@ void decode_kernel(DecodeParams p)
     const int ch1 = FLT || (KT && KB == 8) ? ch0 + 1 : KT ? ch0 + 4 : ch0 + key_pair_step<KB>();
     // (unconditional loads at clamped indices, in one basic block, none waited for before the
     // last is issued; the length first, so that waiting for it leaves the others in flight)
-    const int *len_src = append ? p.pos : p.seq_len;
-    const int len_lane = len_src[min((b & ~63) + lane, p.batch - 1)];
+    const int len_lane = len_src[min((b & ~63) + lane, batch - 1)];
     const int bt_i = split * P + pg_rel;
-    int my_phys = p.block_table[static_cast<long long>(b) * p.max_pages + min(bt_i, pg_lim - 1)];
+    int my_phys = block_table[static_cast<long long>(b) * max_pages + min(bt_i, pg_lim - 1)];
     // q straight from memory in the layouts the lane uses: 8 channels 8*r16 .. +7 of heads
     // 4i + a (the zero terms; their maxima give the per-head exponents) and channels ch0, ch1
     // of every head (the folded key pair); per-token keys also take channels 32J + 2*r16, +1
@@ -949,13 +934,13 @@ void decode_kernel(DecodeParams p)
 #pragma unroll
     for (int i = 0; i < GS; ++i) {
         const long long qi = q0 + min(4 * i + a, G - 1) * kHeadDim + 8 * r16;
-        load_q8<QT>(p.q, qi, qbl[i]);
+        load_q8<QT>(q_in, qi, qbl[i]);
     }
 #pragma unroll
     for (int hh = 0; hh < HS; ++hh) {
         const long long qh = q0 + min(hh, G - 1) * kHeadDim;
-        qwl[hh][0] = load_q<QT>(p.q, qh + ch0);
-        qwl[hh][1] = load_q<QT>(p.q, qh + ch1);
+        qwl[hh][0] = load_q<QT>(q_in, qh + ch0);
+        qwl[hh][1] = load_q<QT>(q_in, qh + ch1);
     }
     if constexpr (KT) {
 #pragma unroll
@@ -963,15 +948,15 @@ void decode_kernel(DecodeParams p)
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
                 const long long qi = q0 + min(4 * i + a, G - 1) * kHeadDim + 32 * J + 2 * r16;
-                qtl[i][J][0] = load_q<QT>(p.q, qi);
-                qtl[i][J][1] = load_q<QT>(p.q, qi + 1);
+                qtl[i][J][0] = load_q<QT>(q_in, qi);
+                qtl[i][J][1] = load_q<QT>(q_in, qi + 1);
             }
     }
     if (bt_i >= pg_lim) my_phys = 0;
     const int L = __builtin_amdgcn_readlane(len_lane, b & 63) + (append ? 1 : 0);
     KVQ_STAMP(8);
 
-    const bool bad_len = (append ? L <= 0 : L < 0) || L > p.max_seq_len || L > kGroup * p.max_pages;
+    const bool bad_len = (append ? L <= 0 : L < 0) || L > p.max_seq_len || L > kGroup * max_pages;
     if (bad_len || L == 0) {
         if (split == 0) {
             const float o = bad_len ? NAN : 0.0f;
@@ -1015,14 +1000,13 @@ void decode_kernel(DecodeParams p)
     // The first page is requested as soon as the block-table ids are in: q, requested before
     // it, is waited for afterwards (the memory counter completes in order), which leaves the
     // page in flight during the q setup below.
-    const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
     // page ids outside the pool mark the sequence bad (NaN outputs) and are read as page 0
     const bool id_bad = lane < n_my && (my_phys < 0 || my_phys >= p.n_pages);
     bool bad_page = __any(id_bad);
     if (id_bad) my_phys = 0;
     auto page_base = [&](int j) -> const uint8_t * {
         const int phys = __builtin_amdgcn_readlane(my_phys, j);
-        return pool + (static_cast<long long>(phys) * p.H + h) * kPageBytes;
+        return pool + (static_cast<long long>(phys) * H + h) * kPageBytes;
     };
     PageRegs<KB, VB> cur, nxt;
     if (n_my > 0) load_page<KB, VB, KM>(cur, page_base(0), lane, ch0, ch1, t0, t1);
@@ -1697,11 +1681,16 @@ void decode_kernel(DecodeParams p)
         const int hh = it / kPerHead, c = (it % kPerHead) * kVec;
         const float *ml_base = p.part_ml + (slot0 * G + hh) * 2;
         load_batch(k, 0);
+        // (slot by slot with constant indices: an index computed at run time would put the
+        // batch arrays in scratch memory)
         auto own = [&](int s0) {
-            if (split >= s0 && split < s0 + kCB) {
-                cmv[k][split - s0] = om[k];
-                clv[k][split - s0] = ol[k];
-                cov[k][split - s0] = oo[k];
+#pragma unroll
+            for (int jb = 0; jb < kCB; ++jb) {
+                if (s0 + jb == split) {
+                    cmv[k][jb] = om[k];
+                    clv[k][jb] = ol[k];
+                    cov[k][jb] = oo[k];
+                }
             }
         };
         own(0);
@@ -1749,10 +1738,17 @@ template <int KB, int VB, int GS, int KM, int NW>
 hipError_t launch_decode_g(const DecodeParams &p, bool q_f32, hipStream_t s)
 {
     dim3 grid(p.H, p.batch, p.n_splits);
+    // the fields the prologue needs first lead as scalar arguments, which the dispatch
+    // preloads into scalar registers (no wait for a kernel-argument load before the first
+    // memory requests); the rest stay in the parameter block
+    const int32_t *len_src = p.pos ? p.pos : p.seq_len;
+    const uint8_t *pool = static_cast<const uint8_t *>(p.pages);
     if (q_f32)
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float, KM, NW>), grid, dim3(64 * NW), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, float, KM, NW>), grid, dim3(64 * NW), 0, s, len_src, p.block_table,
+                           p.q, pool, p.batch, p.max_pages, p.pages_per_split, p.H, p.G, p.pos != nullptr, p);
     else
-        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t, KM, NW>), grid, dim3(64 * NW), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<KB, VB, GS, uint16_t, KM, NW>), grid, dim3(64 * NW), 0, s, len_src,
+                           p.block_table, p.q, pool, p.batch, p.max_pages, p.pages_per_split, p.H, p.G, p.pos != nullptr, p);
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ struct PackParams {
     int batch;
     int max_tokens;
     int max_pages;
+    int heads_fastest;    // set by the launcher: grid (H, pages, batch) rather than (pages, H, batch)
 };
 
 struct AppendParams {

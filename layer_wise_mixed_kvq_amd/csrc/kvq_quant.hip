@@ -72,12 +72,15 @@ __device__ __forceinline__ void encode_page(QuantSmemT<T> &sm, uint8_t *pages, c
         quantize_page<KB, VB, false, KM == kLayerKeysPerToken>(sm, dst);
 }
 
-// grid: (pages covering max_tokens, n_kv_heads, batch)
+// grid: (n_kv_heads, pages covering max_tokens, batch), heads fastest, so that neighbouring
+// workgroups read the H head slices of the same token rows; with more pages than a grid's y
+// extent allows, (pages, n_kv_heads, batch)
 template <int KB, int VB, int KM, typename SrcT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 {
     __shared__ QuantSmemT<SrcT> sm;
-    const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int g = p.heads_fastest ? blockIdx.y : blockIdx.x, h = p.heads_fastest ? blockIdx.x : blockIdx.y;
+    const int b = blockIdx.z;
     const int L = p.seq_len[b];
     if (L < 0 || L > p.max_tokens || L > kGroup * p.max_pages) return;
     const int full = L / kGroup;
@@ -142,11 +145,13 @@ hipError_t launch_pack_m(const PackParams &p, bool src_f32, hipStream_t s)
 {
     const int gx = (p.max_tokens + kGroup - 1) / kGroup;
     if (gx == 0) return hipSuccess;
-    dim3 grid(gx, p.H, p.batch);
+    PackParams q = p;
+    q.heads_fastest = gx <= 65535;
+    const dim3 grid = q.heads_fastest ? dim3(p.H, gx, p.batch) : dim3(gx, p.H, p.batch);
     if (src_f32)
-        hipLaunchKernelGGL((pack_kernel<KB, VB, KM, float>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((pack_kernel<KB, VB, KM, float>), grid, dim3(kThreads), 0, s, q);
     else
-        hipLaunchKernelGGL((pack_kernel<KB, VB, KM, uint16_t>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((pack_kernel<KB, VB, KM, uint16_t>), grid, dim3(kThreads), 0, s, q);
     return hipGetLastError();
 }
 

@@ -26,12 +26,13 @@
 // value scale seen so far, p <= 1).  That keeps the lo parts in the normal fp16 range, where
 // the matrix cores accumulate at full binary32 accuracy.
 //
-// Work decomposition.  One workgroup of four waves per (split, KV head, sequence).  Split
-// s covers pages [s*P, min((s+1)*P, full)), each wave taking every fourth page.  A wave
-// keeps its own online-softmax state; the four are merged in LDS, and every split writes
+// Work decomposition.  One workgroup of NW waves (eight when the launch fits one workgroup
+// per CU, else four) per (split, KV head, sequence).  Split s covers pages
+// [s*P, min((s+1)*P, full)), dealt to its waves in weighted rounds (split_page).  A wave
+// keeps its own online-softmax state; the waves are merged in LDS, and every split writes
 // (m, l, o[128]) per query head to the workspace.  Split 0 also attends over the residual
-// tokens (read into registers at kernel start).  The last split of a (sequence, KV head)
-// to finish -- a device-scope counter -- merges everything:
+// tokens (wave 0, from registers, before its page loop).  The last split of a (sequence,
+// KV head) to finish -- a device-scope counter -- merges everything:
 //   m = max m_s, l = sum 2^(m_s - m) l_s, out = sum 2^(m_s - m) o_s / l, lse = (m + log2 l) ln 2
 // and resets the counter for the next call.  Scores are in log2 units (q carries
 // log2(e)/sqrt(128)).

@@ -859,22 +859,23 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB> &r, const uint8_t *ba
     }
 }
 
-// Pages of a split among its waves, dealt in rounds, round r giving one page to every wave
-// whose weight exceeds r: weight 4 for every wave of an eight-wave workgroup but wave 0 of
-// split 0, which also attends the residual tokens and weighs 2 (a split of 64 pages: 8 per
-// wave, or on split 0 5, 9, 9, 9, 8, 8, 8, 8; the page loop's wave priorities balance the
-// two waves of each SIMD).  Four-wave workgroups (two per CU) deal one page per wave per
-// round.  Returns the split-relative index of the wave's page `j` (increasing in j), in
-// closed form: on split 0 a cycle of four rounds deals 30 pages, rounds 0 and 1 to all eight
-// waves, rounds 2 and 3 to waves 1-7.
+// Pages of a split among its waves.  Four-wave workgroups (two per CU) and every split but
+// split 0 deal them round robin.  On split 0 of an eight-wave workgroup, wave 0 also attends
+// the residual tokens, which costs it about as long as four pages: the first 4 * 7 pages go
+// round robin to waves 1-7, the rest round robin to waves 1-7 and then 0 (a split of 64
+// pages: 4, 9, 9, 9, 9, 8, 8, 8; of 256: 28, then 33 or 32).  Returns the split-relative
+// index of the wave's page `j` (increasing in j).
+constexpr int kResidualPages = 4;
+
 template <int NW>
 __device__ __forceinline__ int split_page(int wave, int j, int split)
 {
     if constexpr (NW != 8) return NW * j + wave;
     if (split != 0) return 8 * j + wave;
-    if (wave == 0) return 30 * (j >> 1) + 8 * (j & 1);
-    const int i = j & 3;
-    return 30 * (j >> 2) + (i < 2 ? 8 * i + wave : 16 + 7 * (i - 2) + wave - 1);
+    constexpr int head = kResidualPages * 7;
+    if (wave == 0) return head + 8 * j + 7;
+    if (j < kResidualPages) return 7 * j + wave - 1;
+    return head + 8 * (j - kResidualPages) + wave - 1;
 }
 
 // KM: the layer code -- integer codes with per-channel or per-token keys (one key group per

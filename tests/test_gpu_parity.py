@@ -24,6 +24,29 @@ def kvq():
     return k
 
 
+def test_pack_long_source_grid(kvq, orc):
+    """Sources longer than 65,535 pages per sequence: the pack launches its page-fastest grid
+    (the heads-fastest one would exceed a grid's y extent). The two short sequences in them
+    are packed bit-exact against the oracle."""
+    import torch
+    c = Case(4, 2, H=2, G=1, lens=[100, 70], seed=77)
+    log(f"pack from a {65536 * 32 + 32}-token source buffer, lens={c.lens.tolist()}")
+    c.oracle_pack(orc)
+    c.device_setup(kvq)
+    t_long = 65536 * 32 + 32
+    k = torch.zeros((c.B, t_long, c.H, 128), dtype=torch.bfloat16, device=c.dev)
+    v = torch.zeros_like(k)
+    k[:, :c.T] = c.k.to(c.dev)
+    v[:, :c.T] = c.v.to(c.dev)
+    kvq.kvq_pack(c.model, 0, c.cache, k, v, c.lens_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cache.pages.cpu().numpy(), c.o_pages)
+    assert live_resid_equal(host_array(c.cache.resid_k), c.o_rk, c.lens)
+    assert live_resid_equal(host_array(c.cache.resid_v), c.o_rv, c.lens)
+    del k, v
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("kb,vb", PAIRS)
 def test_pack_bit_exact(kvq, orc, kb, vb):
     c = Case(kb, vb, H=2, G=1, lens=[77, 64, 5, 0, 200], seed=kb * 10 + vb)
